@@ -1,0 +1,20 @@
+"""FP64 CPU oracle for paged-FP8 MLA decode.
+
+Test infrastructure only: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import it; the HIP library and its binding never do, and
+this package imports nothing from them.  Every function is pinned by tests in
+``tests/test_oracle_*.py`` (see the module docstring of ``mla_oracle`` for the
+definitions and the readings it follows).
+"""
+
+from .mla_oracle import (  # noqa: F401
+    E4M3FN_TABLE,
+    attention_rows,
+    bf16_round,
+    decode,
+    decode_range,
+    e4m3fn_value,
+    gather_dequant,
+    merge_partials,
+    resolve,
+)
