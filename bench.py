@@ -1,0 +1,221 @@
+"""Benchmark: paged-FP8 MLA decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload uniform]
+
+A step is one decode call (main kernel + split combine when the plan splits)
+over one layer of a resident multi-layer paged FP8 cache.  Consecutive steps
+decode consecutive layers, as a model's per-layer calls do; the cache holds
+enough layers (>= 512 MiB) that no step finds its layer in the 256 MB
+Infinity Cache.  Inputs are drawn once (synthetic, seeded) and stay in HBM.
+
+Prints one JSON line: KV tokens/s over the whole step (value), the main
+kernel's achieved rate against its roofline (timed with HIP events recorded
+around the main kernel on the launch stream), and the FP64 oracle timed on
+the host cores over the same workload (one layer) as a reported baseline.
+"""
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA16_TFLOPS = 2500.0      # MI355X dense FP16/BF16 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+MALL_BYTES = 256 << 20
+WORKLOADS = ("uniform", "ragged", "long1", "long4", "spec", "tiny")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make(name, device):
+    from mla_decode_attention_paged_amd import synth
+    if name == "uniform":
+        return synth.uniform(device=device)
+    if name == "ragged":
+        return synth.ragged(device=device)
+    if name == "long1":
+        return synth.long_context(device=device, batch=1)
+    if name == "long4":
+        return synth.long_context(device=device, batch=4)
+    if name == "spec":
+        return synth.speculative(device=device)
+    if name == "tiny":
+        return synth.tiny(device=device, poison=False)
+    raise ValueError(name)
+
+
+def replicate_layers(w, min_bytes):
+    """Give the cache enough layers that consecutive steps never share a cached layer."""
+    import torch
+    NB, KVD, NL, P, HK, D = w.blocks.shape
+    layer_bytes = NB * P * D + w.scales.shape[0] * P * w.scales.shape[-1] * 4
+    n = max(NL, int(math.ceil(min_bytes / layer_bytes)))
+    if n == NL:
+        return w, list(range(NL)) if NL > 1 else [w.layer_idx]
+    src_b = w.blocks[:, :, w.layer_idx:w.layer_idx + 1]
+    src_s = w.scales[:, :, w.layer_idx:w.layer_idx + 1]
+    blocks = src_b.expand(NB, KVD, n, P, HK, D).contiguous()
+    scales = src_s.expand(w.scales.shape[0], KVD, n, P, HK, w.scales.shape[-1]).contiguous()
+    torch.cuda.synchronize()
+    w2 = type(w)(**{**w.__dict__, "blocks": blocks, "scales": scales, "layer_idx": 0})
+    return w2, list(range(n))
+
+
+def algorithmic(w):
+    """Algorithmic bytes and flops of one decode call on workload w."""
+    lens = w.lengths()
+    B, Q, H, D = w.q.shape
+    NG = w.scales.shape[-1]
+    P = w.page_size
+    tables = 1 if w.scales_lookup_table is None else 2
+    kv_bytes = sum(lens) * (D + 4 * NG)
+    table_bytes = sum((L + P - 1) // P for L in lens) * 4 * tables
+    io_bytes = B * Q * H * D * 2 + B * Q * H * 512 * 2 + 4 * B
+    visible = sum(max(0, min(L, L - Q + i + 1)) for L in lens for i in range(Q))
+    flops = visible * H * 2 * (D + 512)
+    return kv_bytes + table_bytes + io_bytes, flops, sum(lens)
+
+
+class HipEvents:
+    """Raw HIP events (hipEvent_t) for timing the main kernel on the launch stream."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e.value)
+
+    def pair(self, i):
+        return self.ev[2 * i], self.ev[2 * i + 1]
+
+    def elapsed_ms(self, i):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), *[ctypes.c_void_p(x) for x in self.pair(i)]) == 0
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(w):
+    """The FP64 oracle, as it stands, timed on the host over one layer of w."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from tests.oracle_inputs import to_numpy
+    from oracle import decode
+    wc = w.to("cpu")
+    q, blocks, scales, lt, slt, cl = to_numpy(wc)
+    blocks = np.ascontiguousarray(blocks[:, :, w.layer_idx:w.layer_idx + 1])
+    scales = np.ascontiguousarray(scales[:, :, w.layer_idx:w.layer_idx + 1])
+    budget_s = 20.0
+    t0 = time.perf_counter()
+    done_tokens = 0
+    done_b = []
+    for b in range(q.shape[0]):
+        decode(q, blocks, scales, lt, slt, cl, 0, w.q_len, w.softmax_scale, batches=[b])
+        done_tokens += int(cl[b])
+        done_b.append(b)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": done_tokens / dt, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"requests {done_b[0]}..{done_b[-1]} of {q.shape[0]} ({done_tokens} cached tokens, "
+                      f"all {w.num_heads} heads, q_len {w.q_len}) of the same workload, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="uniform", choices=WORKLOADS)
+    ap.add_argument("--splits", type=int, default=None, help="explicit split count (default: library plan)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part "
+              "of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_decode_attention_paged_amd import mla_decode_paged_fp8, mla_decode_paged_fp8_plan, lib_path
+
+    dev = torch.device("cuda:0")
+    log(f"bench: workload {args.workload}, library {lib_path()}")
+    w = make(args.workload, dev)
+    w, layers = replicate_layers(w, 2 * MALL_BYTES)
+    alg_bytes, alg_flops, kv_tokens = algorithmic(w)
+    plan = mla_decode_paged_fp8_plan(tuple(w.q.shape), tuple(w.blocks.shape), tuple(w.scales.shape),
+                                     tuple(w.lookup_table.shape), w.q_len, args.splits or 0)
+    log(f"bench: layers {len(layers)}, plan {plan}, kv tokens/step {kv_tokens}")
+    out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+    ev = HipEvents(args.steps)
+
+    def step(i, events=None):
+        mla_decode_paged_fp8(w.q, w.blocks, w.scales, w.lookup_table, w.scales_lookup_table,
+                             w.cache_lengths, layers[i % len(layers)], w.q_len, w.softmax_scale,
+                             out=out, workspace=ws, num_splits=args.splits, main_events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, ev.pair(i))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = [ev.elapsed_ms(i) for i in range(args.steps)]
+    ev.close()
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    tflops = alg_flops / (kern_avg_ms * 1e-3) / 1e12
+    gbs = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
+    log(f"bench: {ms_per_step * 1e3:.1f} us/step, main kernel {kern_avg_ms * 1e3:.1f} us "
+        f"(min {min(kern_ms) * 1e3:.1f}), {tflops:.0f} TFLOP/s, {gbs:.0f} GB/s algorithmic")
+
+    result = {
+        "metric": "MLA decode KV tokens/s + achieved GB/s & MFMA util vs roofline, 1 MI355X",
+        "value": kv_tokens / (ms_per_step * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-kv/f16-mfma/fp32-acc",
+        "data": "synthetic (seeded; N(0,1) x LogNormal(0,0.5) latent rows quantised to E4M3FN)",
+        "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "num_heads": w.num_heads,
+                   "page_size": w.page_size, "granularity": w.granularity,
+                   "kv_tokens_per_step": kv_tokens, "layers_rotated": len(layers), "plan": plan},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_MFMA16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_MFMA16_TFLOPS, "traffic": None,
+                     "kernel": "mla_decode_kernel", "kernel_avg_us": kern_avg_ms * 1e3,
+                     "alg_flops_per_launch": alg_flops, "alg_bytes_per_launch": alg_bytes,
+                     "alg_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the FP64 oracle on the host (bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * mla_paged.h — C ABI of the MI355X (gfx950) paged-FP8 MLA decode library.
+ *
+ * The library computes multi-head latent attention (MLA) decode over a paged
+ * KV cache whose latent rows are stored as FP8 E4M3FN bytes with separately
+ * stored float32 scales.  The storage it reads is the one described on two
+ * Modular API pages:
+ *
+ *   - "generic_get_paged_cache_with_scales" (Mojo function page, section
+ *     "Args"): the blocks tensor [num_blocks, kv_dim, num_layers, page_size,
+ *     num_heads, head_dim]; the scales tensor [num_blocks, kv_dim,
+ *     num_layers, page_size, num_heads, head_dim_granularity]; the page
+ *     lookup table [batch, max_pages]; per-request cache_lengths [batch];
+ *     max_prompt_length (here q_len); and the optional scales lookup table
+ *     [batch, max_pages] for scale pages that carry their own ids (when it
+ *     is absent, scale pages resolve through the value page table).
+ *   - "KVCacheScalesMHAOperand" (Mojo struct page, description and the
+ *     scales_raw_ptr method): per-token K scales kept in the scales field
+ *     when the quantization granularity equals the head size, as Float32.
+ *
+ * The attention step itself (MLA decode with a 576-deep latent key whose
+ * first 512 dims are the value, FP8 KV tiles converted to a 16-bit type for
+ * the tensor-core contractions) is the subject of the "KVLoad2CvtProducer"
+ * page (Mojo struct page, description and "Parameters").
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major
+ *     buffers with the shapes given below; the caller owns them.  The
+ *     library allocates no device memory, keeps no pointer after a call
+ *     returns, and holds no state between calls (reentrant).
+ *   - Work is enqueued asynchronously on `stream`; inputs must stay alive
+ *     and unmodified until the stream has passed the call.
+ *   - Arguments are validated on the host before any HIP call.  On any
+ *     error nothing is launched and the outputs are untouched.
+ *   - Device-side contract (not checked on the device): every page id read
+ *     is < num_blocks (values) or < num_scale_blocks (scales); q_len <=
+ *     cache_lengths[b] <= max_pages * page_size.  Table columns at or past
+ *     ceil(cache_lengths[b] / page_size) are never read, so they may hold
+ *     anything; so may unused slots, pages, layers and kv_dim entries.
+ */
+#ifndef MLA_PAGED_H
+#define MLA_PAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_PAGED_ABI_VERSION 1
+
+/* Status codes.  mla_status_string() returns a static description. */
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer argument is NULL            */
+  MLA_ERR_SHAPE = 2,       /* inconsistent or non-positive sizes             */
+  MLA_ERR_RANGE = 3,       /* layer_idx / q_len / num_splits out of range    */
+  MLA_ERR_UNSUPPORTED = 4, /* sizes valid but not served by these kernels    */
+  MLA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
+  MLA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed     */
+} mla_status;
+
+/*
+ * Sizes of one call.  The tensors are contiguous row-major:
+ *   q      bf16  [batch, q_len, num_q_heads, head_dim]
+ *   blocks u8    [num_blocks, kv_dim, num_layers, page_size, num_kv_heads, head_dim]
+ *                (OCP FP8 E4M3FN bytes; kv index 0 and kv head 0 are read)
+ *   scales f32   [num_scale_blocks, kv_dim, num_layers, page_size, num_kv_heads,
+ *                 scale_groups]   with scale_groups = head_dim / granularity
+ *   lookup_table, scales_lookup_table  u32 [batch, max_pages]
+ *   cache_lengths u32 [batch]
+ *   out    bf16  [batch, q_len, num_q_heads, v_dim]
+ * Served by the kernels: head_dim == 576, v_dim == 512, num_kv_heads == 1,
+ * scale_groups in {1, 9} (granularity 576 or 64), page_size a positive
+ * multiple of 16, num_q_heads * q_len <= 65536.
+ */
+typedef struct {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t v_dim;
+  int64_t num_blocks;
+  int32_t kv_dim;
+  int32_t num_layers;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int64_t num_scale_blocks;
+  int32_t scale_groups;
+  int32_t max_pages;
+} mla_shape;
+
+/* Work decomposition chosen for a call (see mla_decode_paged_fp8_plan). */
+typedef struct {
+  int32_t row_groups;        /* ceil(q_len * num_q_heads / 32)                     */
+  int32_t num_splits;        /* key-range splits per (request, row group)          */
+  int32_t tokens_per_split;  /* keys per split, a multiple of 128                  */
+  int32_t grid;              /* workgroups of the main kernel                      */
+  size_t workspace_bytes;    /* split partials; 0 when num_splits == 1             */
+} mla_plan;
+
+/*
+ * mla_decode_paged_fp8 — attention output of every query row over its
+ * request's paged FP8 cache.
+ *
+ * For request b, query position i < q_len and head h:
+ *   K_j[d] = e4m3fn(blocks[LT[b, j/P], 0, layer_idx, j%P, 0, d])
+ *            * scales[SLT[b, j/P], 0, layer_idx, j%P, 0, d / granularity]
+ *   (SLT = scales_lookup_table when non-NULL, else lookup_table)
+ *   s_j    = softmax_scale * sum_{d<576} q[b,i,h,d] * K_j[d]
+ *   out[b,i,h,:] = bf16( sum_j softmax(s)_j * K_j[0:512] ),
+ * over keys j <= cache_lengths[b] - q_len + i (the q_len newest cached
+ * tokens are the queries themselves, causal among each other).  A row with
+ * no visible key yields zeros.
+ *
+ * workspace: device buffer for split partials, or NULL.  With NULL (or too
+ * small to hold any split plan) the call runs unsplit, which is always
+ * correct.  Use mla_decode_paged_fp8_plan() to learn the size that the
+ * automatic plan wants.  q values must satisfy |q| <= 65504.
+ */
+mla_status mla_decode_paged_fp8(const void* q, const void* blocks, const float* scales,
+                                const uint32_t* lookup_table,
+                                const uint32_t* scales_lookup_table, /* nullable */
+                                const uint32_t* cache_lengths, int32_t layer_idx,
+                                int32_t q_len, float softmax_scale, void* out,
+                                const mla_shape* shape, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Same as mla_decode_paged_fp8 with an explicit split count (0 = automatic).
+ * An explicit count needs a workspace of at least plan.workspace_bytes
+ * (MLA_ERR_WORKSPACE otherwise); num_splits is clamped to the number of
+ * 128-key chunks of max_pages * page_size. */
+mla_status mla_decode_paged_fp8_splits(const void* q, const void* blocks, const float* scales,
+                                       const uint32_t* lookup_table,
+                                       const uint32_t* scales_lookup_table,
+                                       const uint32_t* cache_lengths, int32_t layer_idx,
+                                       int32_t q_len, float softmax_scale, void* out,
+                                       const mla_shape* shape, void* workspace,
+                                       size_t workspace_bytes, int32_t num_splits,
+                                       hipStream_t stream);
+
+/* Same as mla_decode_paged_fp8_splits, and additionally records `main_begin`
+ * and `main_end` (caller-created HIP events, either may be NULL) on `stream`
+ * immediately before and after the main decode kernel, i.e. excluding the
+ * split-combine kernel.  For callers that time the main kernel on its own. */
+mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, const float* scales,
+                                         const uint32_t* lookup_table,
+                                         const uint32_t* scales_lookup_table,
+                                         const uint32_t* cache_lengths, int32_t layer_idx,
+                                         int32_t q_len, float softmax_scale, void* out,
+                                         const mla_shape* shape, void* workspace,
+                                         size_t workspace_bytes, int32_t num_splits,
+                                         hipEvent_t main_begin, hipEvent_t main_end,
+                                         hipStream_t stream);
+
+/* The decomposition a call with these sizes would use (host only, no HIP call
+ * except a cached device-property query).  num_splits = 0 asks for the
+ * automatic plan with an unlimited workspace. */
+mla_status mla_decode_paged_fp8_plan(const mla_shape* shape, int32_t q_len,
+                                     int32_t num_splits, mla_plan* plan);
+
+/*
+ * mla_resolve_pages — debug view of page resolution, computed on the device
+ * with the same routine the decode kernel uses for its tile addresses
+ * (generic_get_paged_cache_with_scales page, "Args": lookup_table and
+ * scales_lookup_table).  For b < batch and t < max_tokens writes
+ *   page[b, t]  = LT[b, t / page_size]   slot[b, t] = t % page_size
+ *   spage[b, t] = SLT[b, t / page_size]  (SLT = LT when NULL)
+ * for t < cache_lengths[b], and 0xFFFFFFFF in all three for t >= it.
+ * Outputs are device u32 [batch, max_tokens].
+ */
+mla_status mla_resolve_pages(const uint32_t* lookup_table, const uint32_t* scales_lookup_table,
+                             const uint32_t* cache_lengths, int32_t batch, int32_t max_pages,
+                             int32_t page_size, int32_t max_tokens, uint32_t* page,
+                             uint32_t* slot, uint32_t* spage, hipStream_t stream);
+
+/* Static, human-readable description of a status code. */
+const char* mla_status_string(mla_status status);
+
+/* MLA_PAGED_ABI_VERSION of the built library. */
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PAGED_H */

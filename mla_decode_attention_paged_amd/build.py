@@ -1,0 +1,73 @@
+"""Build libmla_paged.so for gfx950 with hipcc (in-tree, no JIT cache).
+
+    python -m mla_decode_attention_paged_amd.build
+
+Compiles csrc/mla_decode.hip (kernels + launchers) and csrc/api.cpp (C ABI)
+into mla_decode_attention_paged_amd/libmla_paged.so.  Packed-FP32 VALU
+instructions are disabled for the device code.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(HERE, "libmla_paged.so")
+ARCH = "gfx950"
+
+
+def hipcc_path() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def device_flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    hipcc = hipcc_path()
+    with tempfile.TemporaryDirectory(prefix="mla_build_") as tmp:
+        objs = []
+        for src, lang in (("mla_decode.hip", "hip"), ("api.cpp", "c++")):
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [hipcc, *device_flags(), "-x", lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            if lang == "c++":
+                cmd = [hipcc, "-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
+                       "-c", os.path.join(CSRC, src), "-o", obj]
+            _run(cmd, verbose)
+            objs.append(obj)
+        tmp_out = os.path.join(tmp, "libmla_paged.so")
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_out], verbose)
+        shutil.copyfile(tmp_out, OUT + ".tmp")
+        os.replace(OUT + ".tmp", OUT)
+    return OUT
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}")
+    noise = ("is not a recognized feature", "packed-fp32-ops")
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if ln and not any(n in ln for n in noise)]
+    if verbose and msgs:
+        print("\n".join(msgs))
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI layer (api.cpp) and the gfx950 kernels
+// (mla_decode.hip).  Not installed; the public interface is include/mla_paged.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace mla {
+
+constexpr int kHeadDim = 576;            // latent key depth (512 value dims + 64 rope dims)
+constexpr int kVDim = 512;               // value depth: the first 512 latent dims
+constexpr int kTile = 32;                // keys per MFMA tile
+constexpr int kRows = 32;                // query rows (q position, head) per row group
+constexpr int kWaves = 4;                // waves per workgroup, each streaming its own tiles
+constexpr int kSplitQuantum = kTile * kWaves;   // split lengths are multiples of this
+
+// Everything the main kernel needs, by value.  Offsets are precomputed on the
+// host from the contiguous row-major shapes of the blocks / scales tensors.
+struct DecodeArgs {
+  const uint16_t* q;                 // bf16 bits [B, Q, H, 576]
+  const uint8_t* blocks;             // e4m3fn bytes
+  const float* scales;
+  const uint32_t* lt;                // [B, max_pages]
+  const uint32_t* slt;               // scale page table; == lt when absent
+  const uint32_t* cache_lengths;     // [B]
+  uint16_t* out;                     // bf16 bits [B, Q, H, 512]
+  float* ws_o;                       // split partials O   [B, RG, S, 32, 512] (fp32)
+  float* ws_lse;                     // split partials lse [B, RG, S, 32]      (log2 domain)
+  int64_t page_stride;               // bytes between pages of blocks (kv_dim*num_layers*P*576)
+  int64_t layer_offset;              // bytes to (kv 0, layer_idx, slot 0) inside a page
+  int64_t spage_stride;              // floats between pages of scales
+  int64_t slayer_offset;             // floats to (kv 0, layer_idx, slot 0) inside a scale page
+  int32_t batch, q_len, num_heads, max_pages, page_size;
+  int32_t row_groups, num_splits, tokens_per_split;
+  int32_t grid_units;                // batch * row_groups * num_splits
+  float sm_log2;                     // softmax_scale * log2(e)
+};
+
+size_t partial_bytes(int64_t batch, int64_t row_groups, int64_t num_splits);
+
+// Launch the decode kernel (and the split combine when num_splits > 1).  The
+// optional events are recorded right before / after the decode kernel.
+hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stream,
+                         hipEvent_t main_begin = nullptr, hipEvent_t main_end = nullptr);
+
+hipError_t launch_resolve(const uint32_t* lt, const uint32_t* slt, const uint32_t* cache_lengths,
+                          int batch, int max_pages, int page_size, int max_tokens,
+                          uint32_t* page, uint32_t* slot, uint32_t* spage, hipStream_t stream);
+
+}  // namespace mla

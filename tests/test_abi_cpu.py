@@ -1,0 +1,133 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host (before any HIP call),
+with the documented status codes.  No compute call is made here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_decode_attention_paged_amd import binding
+from mla_decode_attention_paged_amd.binding import MlaPlan, MlaShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_paged.h")
+
+OK, NULL, SHAPE, RANGE, UNSUP, WS, HIP = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mla_status|const char\*|int32_t|size_t)\s+(mla_\w+)\s*\(",
+                                 text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.lib_path()):
+        pytest.fail("libmla_paged.so is not built (run __graft_entry__.build())")
+    return binding.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 7, names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert binding.mla_abi_version() == 1
+    for code in range(7):
+        assert lib.mla_status_string(code).decode()
+    assert lib.mla_status_string(99).decode() == "unknown status"
+
+
+def good_shape(**kw):
+    d = dict(batch=2, num_q_heads=128, head_dim=576, v_dim=512, num_blocks=64, kv_dim=1, num_layers=1,
+             page_size=64, num_kv_heads=1, num_scale_blocks=64, scale_groups=1, max_pages=8)
+    d.update(kw)
+    return MlaShape(**d)
+
+
+def call(lib, shape, *, layer=0, q_len=1, sm=0.07, nulls=(), ws=None, ws_bytes=0, splits=None):
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(7)]
+    for i in nulls:
+        fake[i] = None
+    q, blocks, scales, lt, cl, out, _ = fake
+    args = (q, blocks, scales, lt, None, cl, layer, q_len, ctypes.c_float(sm), out,
+            ctypes.byref(shape) if shape is not None else None, ws, ws_bytes)
+    if splits is None:
+        return lib.mla_decode_paged_fp8(*args, None)
+    return lib.mla_decode_paged_fp8_splits(*args, splits, None)
+
+
+@pytest.mark.parametrize("idx", range(6))
+def test_null_pointers_rejected(lib, idx):
+    assert call(lib, good_shape(), nulls=(idx,)) == NULL
+
+
+def test_null_shape_rejected(lib):
+    assert call(lib, None) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), SHAPE), (dict(num_q_heads=-1), SHAPE), (dict(page_size=0), SHAPE),
+    (dict(scale_groups=5), SHAPE),            # 576 % 5 != 0: granularity must divide head_dim
+    (dict(v_dim=600), SHAPE),
+    (dict(head_dim=512, scale_groups=1), UNSUP), (dict(v_dim=256), UNSUP),
+    (dict(num_kv_heads=2), UNSUP), (dict(scale_groups=3), UNSUP), (dict(page_size=24), UNSUP),
+    (dict(num_q_heads=70000), UNSUP),
+])
+def test_bad_shapes_rejected(lib, kw, code):
+    assert call(lib, good_shape(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layer=1), RANGE), (dict(layer=-1), RANGE), (dict(q_len=0), RANGE),
+    (dict(sm=0.0), RANGE), (dict(sm=float("nan")), RANGE), (dict(splits=-2), RANGE),
+])
+def test_bad_ranges_rejected(lib, kw, code):
+    assert call(lib, good_shape(), **kw) == code
+
+
+def test_explicit_splits_need_workspace(lib):
+    assert call(lib, good_shape(max_pages=64), splits=4) == WS
+    assert call(lib, good_shape(max_pages=64), splits=4, ws=ctypes.c_void_p(0x9000), ws_bytes=16) == WS
+
+
+def plan(lib, shape, q_len=1, splits=0):
+    p = MlaPlan()
+    st = lib.mla_decode_paged_fp8_plan(ctypes.byref(shape), q_len, splits, ctypes.byref(p))
+    return st, p
+
+
+def test_plan_covers_the_key_range(lib):
+    for B, H, Q, maxp, P in [(16, 128, 1, 64, 64), (1, 128, 1, 1024, 128), (64, 128, 1, 128, 64),
+                             (128, 128, 4, 512, 64), (2, 16, 1, 7, 16)]:
+        st, p = plan(lib, good_shape(batch=B, num_q_heads=H, max_pages=maxp, page_size=P,
+                                     num_blocks=maxp * B), q_len=Q)
+        assert st == OK
+        assert p.row_groups == (Q * H + 31) // 32
+        assert p.tokens_per_split % 128 == 0
+        assert p.num_splits * p.tokens_per_split >= maxp * P
+        assert (p.num_splits - 1) * p.tokens_per_split < maxp * P
+        assert p.grid % 8 == 0 and p.grid >= B * p.row_groups * p.num_splits
+        if p.num_splits == 1:
+            assert p.workspace_bytes == 0
+        else:
+            units = B * p.row_groups * p.num_splits
+            assert p.workspace_bytes == units * 32 * 512 * 4 + units * 32 * 4
+
+
+def test_plan_explicit_splits_clamped(lib):
+    st, p = plan(lib, good_shape(max_pages=2, page_size=64), splits=50)   # 128 keys -> 1 chunk
+    assert st == OK and p.num_splits == 1
+
+
+def test_resolve_rejects_bad_args(lib):
+    f = ctypes.c_void_p(0x1000)
+    assert lib.mla_resolve_pages(None, None, f, 2, 4, 16, 64, f, f, f, None) == NULL
+    assert lib.mla_resolve_pages(f, None, f, 0, 4, 16, 64, f, f, f, None) == SHAPE
+    assert lib.mla_resolve_pages(f, None, f, 2, 4, 16, 0, f, f, f, None) == SHAPE

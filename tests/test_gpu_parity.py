@@ -1,0 +1,154 @@
+"""GPU parity: the HIP path (through the C ABI) against the FP64 oracle.
+
+Gate (floating point): e = |gpu - bf16(oracle)| / max(1, |oracle|), max e <=
+1e-2 and mean e <= 1e-3 on the bf16 outputs.  Index work (page / slot / scale
+page resolution) is compared bit-exactly.  Sizes here are ones the oracle
+finishes in seconds while still spanning several 32-key tiles, several waves
+and ragged tails; the full-size workloads are checked on sampled requests in
+test_gpu_fullsize.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mla_decode_attention_paged_amd import mla_resolve_pages
+from mla_decode_attention_paged_amd.synth import make_workload, tiny, u32_numpy
+from oracle import resolve
+from tests.gpu_helpers import check_gate, run_gpu, say
+from tests.oracle_inputs import oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(gpu_device, *args, **kw):
+    kw.setdefault("device", gpu_device)
+    return make_workload(*args, **kw)
+
+
+# ------------------------------------------------------------------ resolution
+@pytest.mark.parametrize("page,indep,lengths", [
+    (16, False, [37, 100]), (64, True, [1, 64, 65, 4000]), (128, True, [131, 9000]),
+])
+def test_resolve_bit_exact(gpu_device, page, indep, lengths):
+    say("resolve", page, indep, lengths)
+    w = _w(gpu_device, len(lengths), 4, lengths, page, 64, independent_scales=indep,
+           spare_blocks=3, spare_scale_blocks=5, unused_table_id=0xFFFFFFFF, seed=page)
+    max_tokens = max(lengths) + 40
+    pg, sl, sp = mla_resolve_pages(w.lookup_table, w.scales_lookup_table, w.cache_lengths, page, max_tokens)
+    torch.cuda.synchronize()
+    lt = u32_numpy(w.lookup_table)
+    slt = None if w.scales_lookup_table is None else u32_numpy(w.scales_lookup_table)
+    rows = resolve(lt, slt, lengths, page)
+    got = [u32_numpy(t) for t in (pg, sl, sp)]
+    for b, L in enumerate(lengths):
+        for k in range(3):
+            assert np.array_equal(got[k][b, :L].astype(np.int64), rows[b][:, k]), (b, k)
+            assert (got[k][b, L:] == 0xFFFFFFFF).all()
+
+
+# ------------------------------------------------------------------ parity, small
+def test_tiny_workload(gpu_device):
+    say("tiny (B=2, H=16, L={37,100}, P=16, per-token scales, NaN poison)")
+    w = tiny(device=gpu_device, poison=True)
+    check_gate(run_gpu(w), oracle_decode(w), "tiny")
+
+
+@pytest.mark.parametrize("gran", [576, 64])
+def test_128_heads_ragged_lengths(gpu_device, gran):
+    say("128 heads ragged", gran)
+    w = _w(gpu_device, 4, 128, [1, 77, 1000, 33], 64, gran, independent_scales=gran == 64,
+           spare_blocks=2, spare_scale_blocks=3, seed=21 + gran, poison=True,
+           unused_table_id=0xFFFFFFFF)
+    check_gate(run_gpu(w), oracle_decode(w), f"ragged g{gran}")
+
+
+@pytest.mark.parametrize("page", [16, 128])
+def test_page_sizes(gpu_device, page):
+    say("page size", page)
+    w = _w(gpu_device, 2, 128, [513, 250], page, 576, seed=31 + page, poison=True)
+    check_gate(run_gpu(w), oracle_decode(w), f"page {page}")
+
+
+def test_causal_four_queries_layer_select(gpu_device):
+    say("q_len 4, layer 2 of 4, group scales, own scale table")
+    w = _w(gpu_device, 3, 128, [4, 70, 1500], 64, 64, q_len=4, num_layers=4, layer_idx=2,
+           independent_scales=True, spare_blocks=2, spare_scale_blocks=2, seed=41, poison=True)
+    check_gate(run_gpu(w), oracle_decode(w), "causal q4")
+
+
+def test_rows_mixing_query_positions(gpu_device):
+    """16 heads x 4 queries: one 32-row group holds two query positions."""
+    say("H=16, q_len 4")
+    w = _w(gpu_device, 2, 16, [9, 300], 16, 576, q_len=4, seed=51, poison=True)
+    check_gate(run_gpu(w), oracle_decode(w), "h16 q4")
+
+
+def test_odd_head_count(gpu_device):
+    say("H=40 (partial row group)")
+    w = _w(gpu_device, 2, 40, [3, 200], 64, 64, seed=52, poison=True)
+    check_gate(run_gpu(w), oracle_decode(w), "h40")
+
+
+def test_empty_request_gives_zeros(gpu_device):
+    say("L = 0 request")
+    w = _w(gpu_device, 3, 128, [0, 5, 0], 64, 576, seed=61, poison=True)
+    out = run_gpu(w)
+    assert (out[0] == 0).all() and (out[2] == 0).all()
+    check_gate(out[1:2], oracle_decode(w)[1:2], "L=0 neighbours")
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7])
+def test_forced_splits(gpu_device, splits):
+    say("forced splits", splits)
+    w = _w(gpu_device, 2, 128, [3000, 700], 64, 64, independent_scales=True, seed=71, poison=True)
+    ref = oracle_decode(w)
+    out = run_gpu(w, num_splits=splits)
+    check_gate(out, ref, f"splits {splits}")
+    base = run_gpu(w, num_splits=1)
+    check_gate(base, ref, "splits 1")
+
+
+# ------------------------------------------------------------------ invariances on the GPU
+def test_page_permutation_bitwise(gpu_device):
+    say("permutation invariance")
+    w = _w(gpu_device, 2, 128, [200, 90], 16, 64, independent_scales=True, spare_blocks=5,
+           spare_scale_blocks=5, seed=81, poison=True)
+    out1 = run_gpu(w, num_splits=1)
+    NB = w.blocks.shape[0]
+    perm = torch.randperm(NB, generator=torch.Generator().manual_seed(1)).to(gpu_device)
+    blocks2 = torch.empty_like(w.blocks)
+    blocks2[perm] = w.blocks
+    lt = w.lookup_table.to(torch.int64) & 0xFFFFFFFF
+    lt2 = perm[lt.clamp(max=NB - 1)].to(torch.int32)
+    w2 = type(w)(**{**w.__dict__, "blocks": blocks2, "lookup_table": lt2.contiguous()})
+    out2 = run_gpu(w2, num_splits=1)
+    assert torch.equal(out1, out2)
+
+
+def test_shared_table_equals_independent_copy(gpu_device):
+    say("shared vs independent table")
+    w = _w(gpu_device, 2, 128, [130, 400], 64, 576, seed=82, poison=True)
+    out1 = run_gpu(w)
+    w2 = type(w)(**{**w.__dict__, "scales_lookup_table": w.lookup_table.clone()})
+    out2 = run_gpu(w2)
+    assert torch.equal(out1, out2)
+
+
+def test_reference_max_too_low_redo(gpu_device):
+    """First tiles nearly zero, later keys huge: P' against the first tile's max
+    would overflow f16, so the waves repeat their keys against the exact max."""
+    say("overflow redo path")
+    w = _w(gpu_device, 2, 128, [1500, 700], 64, 576, seed=91, poison=True)
+    lt = w.lookup_table.to(torch.int64).cpu()
+    P = w.page_size
+    for b, L in enumerate(w.lengths()):
+        for t in range(L):
+            page, slot = int(lt[b, t // P]), t % P
+            # keys 0..127 (first tiles of all four waves of split 0) tiny, others large
+            f = 1e-3 if t < 128 else 40.0
+            w.scales[page, 0, 0, slot, 0, :] *= f
+    torch.cuda.synchronize()
+    ref = oracle_decode(w)
+    check_gate(run_gpu(w, num_splits=1), ref, "redo")
+    check_gate(run_gpu(w), ref, "redo, auto plan")

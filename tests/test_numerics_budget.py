@@ -1,0 +1,127 @@
+"""Rounding budget of the GPU recipe, emulated on the CPU against the oracle.
+
+The HIP kernel computes: q in f16 (exact for bf16 inputs of normal magnitude),
+E4M3FN codes widened to f16 (exact), QK^T with fp32 accumulation, the fp32
+scale applied to score columns (one scale per key) or to 64-deep group partial
+sums, an fp32 base-2 softmax, P' = f16(p * scale) against the unscaled FP8
+value codes, fp32 accumulation of P'V and of the row sums, and one final
+bf16 rounding of O / l.  This test emulates exactly those roundings in numpy
+(accumulations in float64 then rounded to float32, which is finer than the
+hardware's fp32 sums and does not change the verdict) and checks the parity
+gate against the oracle: e = |gpu - bf16(oracle)| / max(1, |oracle|) with
+max e <= 1e-2 and mean e <= 1e-3.
+
+It also records why cheaper roundings are not used: a bf16 P' does not pass,
+and neither does dequantising K to f16 with 64-wide group scales (the f16
+rounding of the scaled key, correlated over each 64-deep group, moves large
+base-2 scores by ~1e-2).
+"""
+
+import numpy as np
+import pytest
+
+from mla_decode_attention_paged_amd.synth import make_workload
+from oracle import E4M3FN_TABLE, bf16_round, gather_dequant, resolve
+from tests.oracle_inputs import gate_stats, oracle_decode, to_numpy
+
+LOG2E = 1.4426950408889634
+
+
+def _f16(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def _bf16(x):
+    return bf16_round(np.asarray(x, dtype=np.float64))
+
+
+def emulate(w, p_round="f16", k_mode="exact"):
+    """Emulated kernel output (float64 holding bf16 values) for workload w."""
+    q, blocks, scales, lt, slt, cl = to_numpy(w)
+    B, Q, H, D = q.shape
+    P = blocks.shape[3]
+    NG = scales.shape[-1]
+    G = D // NG
+    sm_log2 = _f32(np.float32(w.softmax_scale) * np.float32(LOG2E))
+    out = np.zeros((B, Q, H, 512))
+    for b in range(B):
+        L = int(cl[b])
+        rows = resolve(lt[b:b + 1], None if slt is None else slt[b:b + 1], [L], P)[0]
+        codes = blocks[rows[:, 0], 0, w.layer_idx, rows[:, 1], 0, :]            # [L, D]
+        sc = scales[rows[:, 2], 0, w.layer_idx, rows[:, 1], 0, :].astype(np.float64)   # [L, NG]
+        Kq = E4M3FN_TABLE[codes]                                                # exact in f16
+        for i in range(Q):
+            n = L - Q + i + 1
+            if n <= 0:
+                continue
+            q16 = _f16(q[b, i])                                                  # [H, D]
+            if NG == 1:
+                S = _f32(q16 @ Kq[:n].T)                                         # fp32 accumulate
+                x = _f32(_f32(S * sc[:n, 0][None, :]) * sm_log2)
+            elif k_mode == "exact":
+                S = np.zeros((H, n))
+                for g in range(NG):
+                    T = _f32(q16[:, g * G:(g + 1) * G] @ Kq[:n, g * G:(g + 1) * G].T)
+                    S = _f32(S + T * sc[:n, g][None, :])
+                x = _f32(S * sm_log2)
+            else:   # K dequantised to f16 before QK (not used by the kernel)
+                K16 = _f16(Kq[:n] * _f16(np.repeat(sc[:n], G, axis=1)))
+                S = _f32(q16 @ K16.T)
+                x = _f32(S * sm_log2)
+            m = x.max(axis=1, keepdims=True)
+            p = _f32(np.exp2(x - m))
+            l = _f32(p.sum(axis=1))
+            rnd = _f16 if p_round == "f16" else _bf16
+            if NG == 1:
+                Pp = rnd(_f32(p * sc[:n, 0][None, :]))
+                O = _f32(Pp @ Kq[:n, :512])
+            else:
+                O = np.zeros((H, 512))
+                for g in range(8):
+                    Pp = rnd(_f32(p * sc[:n, g][None, :]))
+                    O[:, g * 64:(g + 1) * 64] = _f32(Pp @ Kq[:n, g * 64:(g + 1) * 64])
+            out[b, i] = _bf16(_f32(O / l[:, None]))
+    return out
+
+
+CASES = {
+    "tiny_per_token": dict(batch=2, num_heads=16, cache_lengths=[37, 100], page_size=16,
+                           granularity=576, spare_blocks=6, seed=0),
+    "uniform_like": dict(batch=2, num_heads=32, cache_lengths=[4096, 4096], page_size=64,
+                         granularity=576, seed=1001),
+    "ragged_group64": dict(batch=3, num_heads=32, cache_lengths=[1, 2500, 8192], page_size=64,
+                           granularity=64, independent_scales=True, seed=2001),
+    "spec_group64": dict(batch=1, num_heads=16, cache_lengths=[3000], page_size=64,
+                         granularity=64, q_len=4, num_layers=4, layer_idx=2,
+                         independent_scales=True, seed=4001),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_kernel_recipe_meets_gate(name):
+    w = make_workload(poison=False, **CASES[name])
+    ref = oracle_decode(w)
+    st = gate_stats(emulate(w, "f16", "exact"), ref)
+    print(name, st)
+    assert st["max_norm"] <= 1e-2 and st["mean_norm"] <= 1e-3, st
+
+
+def test_bf16_probabilities_miss_the_gate():
+    """The cheaper bf16 P' breaks the gate on a long per-token workload."""
+    w = make_workload(poison=False, **CASES["uniform_like"])
+    ref = oracle_decode(w)
+    st = gate_stats(emulate(w, "bf16", "exact"), ref)
+    print("bf16 P'", st)
+    assert st["max_norm"] > 1e-2 or st["mean_norm"] > 1e-3, st
+
+
+def test_f16_dequantised_keys_miss_the_gate_with_group_scales():
+    w = make_workload(poison=False, **CASES["ragged_group64"])
+    ref = oracle_decode(w)
+    st = gate_stats(emulate(w, "f16", "k16"), ref)
+    print("K16", st)
+    assert st["max_norm"] > 1e-2 or st["mean_norm"] > 1e-3, st
