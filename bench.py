@@ -29,6 +29,15 @@ PEAK_MFMA16_TFLOPS = 2500.0      # MI355X dense FP16/BF16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 MALL_BYTES = 256 << 20
 WORKLOADS = ("uniform", "ragged", "long1", "long4", "spec", "tiny")
+KERNEL_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "mla_decode.hip")
+
+# HBM bytes per main-kernel launch read from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE on `bench.py --steps 5 --warmup 2 --no-cpu-baseline`, each
+# divided by the factor the same counter shows for a plain copy of known size
+# (`bench.py --calibrate-copy`).  Keyed by the SHA-256 of the kernel source the
+# counters were taken on: any later edit of the kernel makes the figure stale,
+# and bench then reports traffic as null.
+MEASURED_TRAFFIC = {}
 
 
 def log(*a):
@@ -111,6 +120,23 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def kernel_digest():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def calibrate_copy(n_bytes=1 << 30, reps=3):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibrate-copy: {reps} copies of {n_bytes} bytes (read {n_bytes}, write {n_bytes} each)")
+
+
 def cpu_baseline(w):
     """The FP64 oracle, as it stands, timed on the host over one layer of w."""
     import numpy as np
@@ -121,21 +147,24 @@ def cpu_baseline(w):
     q, blocks, scales, lt, slt, cl = to_numpy(wc)
     blocks = np.ascontiguousarray(blocks[:, :, w.layer_idx:w.layer_idx + 1])
     scales = np.ascontiguousarray(scales[:, :, w.layer_idx:w.layer_idx + 1])
-    budget_s = 20.0
+    # run requests in order, cycling, until about 10 s of CPU work is done
+    budget_s = 10.0
     t0 = time.perf_counter()
-    done_tokens = 0
-    done_b = []
-    for b in range(q.shape[0]):
+    done_tokens, calls = 0, 0
+    B = q.shape[0]
+    while True:
+        b = calls % B
         decode(q, blocks, scales, lt, slt, cl, 0, w.q_len, w.softmax_scale, batches=[b])
         done_tokens += int(cl[b])
-        done_b.append(b)
+        calls += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": done_tokens / dt, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"requests {done_b[0]}..{done_b[-1]} of {q.shape[0]} ({done_tokens} cached tokens, "
-                      f"all {w.num_heads} heads, q_len {w.q_len}) of the same workload, {dt:.1f} s wall"}
+            "sample": f"{calls} single-request oracle calls cycling over the {B} requests of one layer of the "
+                      f"same workload ({done_tokens} cached tokens, all {w.num_heads} heads, q_len {w.q_len}), "
+                      f"{dt:.1f} s wall"}
 
 
 def main():
@@ -146,12 +175,17 @@ def main():
     ap.add_argument("--workload", default="uniform", choices=WORKLOADS)
     ap.add_argument("--splits", type=int, default=None, help="explicit split count (default: library plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part "
               "of this build", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import torch
     from mla_decode_attention_paged_amd import mla_decode_paged_fp8, mla_decode_paged_fp8_plan, lib_path
 
@@ -206,7 +240,8 @@ def main():
                    "page_size": w.page_size, "granularity": w.granularity,
                    "kv_tokens_per_step": kv_tokens, "layers_rotated": len(layers), "plan": plan},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_MFMA16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_MFMA16_TFLOPS, "traffic": None,
+                     "frac": tflops / PEAK_MFMA16_TFLOPS,
+                     "traffic": MEASURED_TRAFFIC.get(kernel_digest(), {}).get(w.name),
                      "kernel": "mla_decode_kernel", "kernel_avg_us": kern_avg_ms * 1e3,
                      "alg_flops_per_launch": alg_flops, "alg_bytes_per_launch": alg_bytes,
                      "alg_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS},

@@ -5,25 +5,24 @@
 // "Args": blocks / scales tensors, lookup_table, optional scales_lookup_table,
 // cache_lengths) and the "KVCacheScalesMHAOperand" page (per-token Float32
 // scales kept in the scales field).  The "KVLoad2CvtProducer" page describes a
-// Blackwell pipeline that stages FP8 KV tiles in shared memory and converts
-// them to a 16-bit type for the tensor cores; on CDNA4 the same idea becomes:
+// Blackwell pipeline in which producer warps stage FP8 KV tiles in shared
+// memory, convert them to a 16-bit type, and hand them to MMA warps.  On CDNA4:
 //
-//   * one workgroup = 4 waves on one group of 32 query rows (q position, head);
-//     each wave streams its own 32-key tiles through a private, double-buffered
-//     LDS tile filled by direct global->LDS dwordx4 loads (no VGPR staging);
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_f16: FP8 bytes are widened to f16
-//     exactly in registers (scale 1.0 conversion); q (bf16) is held in f16,
-//     which is exact for 2^-14 <= |q| <= 65504; the fp32 scale is applied to
-//     score columns (one scale per key) or per 64-deep group partial sums;
-//   * softmax in fp32, base 2, against a per-wave reference max taken from the
-//     wave's first tile: the accumulators are never rescaled (no VALU touches
-//     them in the loop, so they stay in AGPRs); P' may exceed 1, and a wave
-//     whose P' overflowed f16 repeats its keys once against the exact max;
-//   * O = P' V on the same MFMA, with P' = f16(p * scale) and V read from the
-//     same LDS tile through ds_read_b64_tr_b8 (8 keys of one column per lane);
-//   * the 4 waves merge (m, l, O) through LDS; a workgroup either writes the
-//     final bf16 rows or, when a request's keys are split across workgroups,
-//     an fp32 partial (O / l, log2-sum-exp) merged by mla_combine.
+//   * FP8 key bytes go from HBM straight into LDS (global_load_lds_dwordx4,
+//     no VGPR staging) and are widened in registers right before the MFMAs
+//     that use them: to bf16 for QK^T (exact; q is bf16 as given, so every
+//     product is exact and the fp32 accumulation is the only rounding) and to
+//     f16 for PV, with P' = f16(p * scale).  gfx950's block-scaled FP8 MFMA
+//     would skip the widening, but its internal accumulation keeps only about
+//     12 bits of the products' magnitude sum, which large scores turn into
+//     visible softmax weight errors; an FP8 P' is not accurate enough either;
+//   * the roles are split between waves (two score waves, two value waves) so
+//     that each keeps its operands in registers: q for the score waves, the
+//     O accumulators for the value waves;
+//   * the softmax is online, base 2, in fp32, with lazy rescaling;
+//   * a workgroup either writes final bf16 rows or, when a request's keys are
+//     split across workgroups, an fp32 partial (O / l, log2-sum-exp) that
+//     mla_combine merges.
 #include <hip/hip_runtime.h>
 
 #include "mla_internal.h"
@@ -45,15 +44,6 @@ typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 constexpr int kTileBytes = kTile * kHeadDim;   // 18432: one 32-key FP8 tile
 constexpr float kNegInf = -__builtin_inff();
 
-template <int NG>
-struct Layout {
-  // scales per tile in LDS: NG == 1 -> 64 floats (lanes 32..63 load duplicates),
-  // NG == 9 -> [group][key] 9 x 32 floats plus a 32-float tail for the last load.
-  static constexpr int kScaleBytes = NG == 1 ? 256 : 1280;
-  static constexpr int kWaveBytes = 2 * kTileBytes + 2 * kScaleBytes + 128;   // + row-factor scratch
-  static constexpr int kTotal = kWaves * kWaveBytes;
-};
-static_assert(Layout<9>::kTotal <= 160 * 1024, "LDS budget");
 
 // ---------------------------------------------------------------- page resolution
 // Token t of request b: value page = LT[b, t / P], slot = t % P, scale page =
@@ -82,6 +72,16 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t lo, uint32_t hi) {
   const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
   const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
@@ -136,14 +136,53 @@ __device__ __forceinline__ void lds_dma4(const void* gsrc, LDS_AS void* ldst) {
 __device__ __forceinline__ constexpr int tile_key(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
 // ---------------------------------------------------------------- the decode kernel
+//
+// Workgroup = 4 waves on one group of 32 query rows (q position, head) and one
+// key range [t_lo, t_hi) of one request.  The key range is cut into 32-key
+// tiles; a "step" is two consecutive tiles.  Roles:
+//
+//   score waves S0, S1 (waves 0, 1): S_w owns tile 2i + w of step i.  It holds
+//     q (bf16) for all 32 rows in registers, computes S^T = K Q^T on
+//     v_mfma_f32_32x32x16_bf16 with the keys widened FP8 -> bf16 as they come
+//     out of LDS, applies the key scales in fp32, runs the
+//     online softmax (its own row sums against a reference max that follows
+//     the partner score wave's and moves lazily), and hands P' (f16) and the
+//     tile's reference max per row to the value waves via LDS.
+//   value waves V0, V1 (waves 2, 3): V_c owns output columns [256c, 256c+256)
+//     and one accumulator O, and computes O += P' V on
+//     v_mfma_f32_32x32x16_f16 for both tiles of a step, one step behind the
+//     score waves, with V read from the same LDS tile through
+//     ds_read_b64_tr_b8.  When a tile's reference differs from O's, the
+//     smaller side is scaled to the larger (rare: references move lazily).
+//
+// Tiles arrive by direct global->LDS dwordx4 loads that all four waves issue
+// one step ahead; a tile buffer lives three steps (loaded, scored, consumed),
+// and one workgroup barrier per step orders the hand-offs.
+template <int NG>
+struct Layout {
+  static constexpr int kScaleBytes = NG == 1 ? 256 : 1280;      // per tile
+  static constexpr int kPBytes = NG == 1 ? 2048 : 4096;         // P' (f16) or p (fp32) per tile
+  static constexpr int kTiles = 0;                               // 3 steps x 2 tiles
+  static constexpr int kScales = kTiles + 6 * kTileBytes;
+  static constexpr int kP = kScales + 6 * kScaleBytes;           // 2 steps x 2 tiles
+  static constexpr int kAlpha = kP + 4 * kPBytes;                // 2 steps x 2 tiles x 32 row maxima
+  static constexpr int kAlphaBytes = 128;
+  static constexpr int kStats = kAlpha + 4 * kAlphaBytes;        // m, l of both score waves
+  static constexpr int kMO = kStats + 4 * kRows * 4;             // reference max of each value wave's O
+  static constexpr int kTotal = kMO + 2 * kRows * 4;
+};
+static_assert(Layout<9>::kTotal <= 160 * 1024, "LDS budget");
+
 template <int NG>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 mla_decode_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   using LY = Layout<NG>;
+  LDS_AS char* const L0 = (LDS_AS char*)lds;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int g = lane >> 5;          // lane half
   const int n = lane & 31;          // MFMA column / row within the half
 
@@ -167,79 +206,45 @@ mla_decode_kernel(DecodeArgs a) {
   if (split >= nsplit_eff) return;             // no keys here; nothing to write
   const int t_lo = split * T;
   const int t_hi = min(L, t_lo + T);
-
+  const int ntiles = (t_hi - t_lo + kTile - 1) / kTile;
+  const int nsteps = (ntiles + 1) / 2;
   const int rows_total = a.q_len * a.num_heads;
 
-  // ---- per-lane row bookkeeping (S^T layout: lane column n is row rg*32 + n)
-  const int my_row = rg * kRows + n;
-  const bool row_ok = my_row < rows_total;
-  const int my_i = row_ok ? my_row / a.num_heads : 0;
-  // keys visible to this row: j < L - Q + i + 1, clipped to this split
-  int lim = row_ok ? min(L - a.q_len + my_i + 1, t_hi) : t_hi;
-  // the earliest limit over the wave's real rows decides whether a tile needs masking
-  int lim_min = row_ok ? lim : 0x7fffffff;
-  for (int off = 16; off >= 1; off >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
-  lim_min = __builtin_amdgcn_readfirstlane(min(lim_min, __shfl_xor(lim_min, 32)));
+  // ---- LDS regions
+  auto tile_buf = [&](int step, int tt) __attribute__((always_inline)) {
+    return L0 + LY::kTiles + ((step % 3) * 2 + tt) * kTileBytes;
+  };
+  auto scale_buf = [&](int step, int tt) __attribute__((always_inline)) {
+    return L0 + LY::kScales + ((step % 3) * 2 + tt) * LY::kScaleBytes;
+  };
+  auto p_buf = [&](int step, int tt) __attribute__((always_inline)) {
+    return L0 + LY::kP + ((step & 1) * 2 + tt) * LY::kPBytes;
+  };
+  auto alpha_buf = [&](int step, int tt) __attribute__((always_inline)) {
+    return (LDS_AS float*)(L0 + LY::kAlpha + ((step & 1) * 2 + tt) * LY::kAlphaBytes);
+  };
 
-  // ---- Q fragments (B operand of S^T = K Q^T), f16, held for the whole key range.
-  // k-step s = 2u + v covers depth d = 32u + 16g + 8v + e, e < 8.
-  f16x8 qf[36];
-  {
-    const uint16_t* qrow = a.q + (size_t)(row_ok ? my_row : 0) * kHeadDim + (size_t)b * rows_total * kHeadDim;
-#pragma unroll
-    for (int u = 0; u < 18; ++u) {
-      const u32x4 w0 = *(const u32x4*)(qrow + 32 * u + 16 * g);
-      const u32x4 w1 = *(const u32x4*)(qrow + 32 * u + 16 * g + 8);
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const u32x4 w = v ? w1 : w0;
-        f16x8 f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float lo = bf16_bits_to_f32(w[k] & 0xffffu);
-          const float hi = bf16_bits_to_f32(w[k] >> 16);
-          f[2 * k] = row_ok ? (_Float16)lo : (_Float16)0.0f;
-          f[2 * k + 1] = row_ok ? (_Float16)hi : (_Float16)0.0f;
-        }
-        qf[2 * u + v] = f;
-      }
-    }
-  }
-
-  // ---- LDS regions of this wave (address space 3, 32-bit addressing)
-  LDS_AS char* const lds0 = (LDS_AS char*)lds;
-  LDS_AS char* const wbase = lds0 + wave * LY::kWaveBytes;
-
-  // Global->LDS tile layout: 18 blocks of 1 KiB, block i = 9*(key/16) + col/64;
-  // inside a block, 16-byte slot 4*(key%16) + ((c%4) ^ ((key%16)/4 % 4)) holds
-  // bytes [16c, 16c+16) of that key, c = 16-byte column index.  The XOR spreads
-  // the 16 keys of an MFMA read over all LDS banks.
+  // ---- tile loads.  Global->LDS tile layout: 18 blocks of 1 KiB, block
+  // 9*(key/16) + col/64; inside a block, 16-byte slot 4*(key%16) +
+  // ((c%4) ^ ((key%16)/4 % 4)) holds bytes [16c, 16c+16) of that key (c = 16-byte
+  // column).  The XOR spreads the 16 keys of an MFMA read over all LDS banks.
   const int ld_key = lane >> 2;                                   // key % 16 loaded by this lane
   const int ld_col = (lane & 3) ^ ((lane >> 4) & 3);              // 16B column % 4 loaded by this lane
-  const uint32_t ld_off = (uint32_t)ld_key * kHeadDim + 16u * ld_col;   // + 64*(col/4) per block
-
-  // K read (A operand): lane (key n, half g) reads 16B column c = 2u + g
-  const uint32_t kread[2] = {
-      (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((0 + g) ^ ((n >> 2) & 3)))),
-      (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((2 + g) ^ ((n >> 2) & 3))))};
-  // V read (B operand via transpose read): provider lane p = 2k + h of each 16-lane
-  // group addresses key tau(g,k) = 4g + (k&3) + 8(k>>2) at column 32nb + 16q + 8h.
-  const int vq = (lane >> 4) & 1, vk = (lane & 15) >> 1, vh = lane & 1;
-  const int vtau = 4 * g + (vk & 3) + 8 * (vk >> 2);
-  const uint32_t vread[2] = {
-      (uint32_t)(16 * (4 * vtau + ((0 + vq) ^ ((vtau >> 2) & 3))) + 8 * vh),
-      (uint32_t)(16 * (4 * vtau + ((2 + vq) ^ ((vtau >> 2) & 3))) + 8 * vh)};
-
   const uint8_t* layer_base = a.blocks + a.layer_offset;
   const float* slayer_base = a.scales + a.slayer_offset;
 
-  // Issue the global->LDS loads of the tile starting at key t0 into buffer `buf`.
-  // Keys at or past t_hi are never read: their lanes re-load the last valid key
-  // (finite data that the softmax masks out), so stale or NaN-holding slots,
-  // pages and table columns past a request's length stay untouched.
-  auto issue_tile = [&](int t0, int buf) __attribute__((always_inline)) {
+  // Wave w loads half (w & 1) of tile (w >> 1) of `step` (9 blocks), and the
+  // scales of that tile when it loads half 0.  Keys at or past t_hi are never
+  // read: their lanes re-load the last valid key (finite data that the softmax
+  // masks out), so slots, pages and table columns past a request's length stay
+  // untouched.
+  auto issue_step = [&](int step) __attribute__((always_inline)) {
+    const int tt = wave >> 1, hb = wave & 1;
+    const int j = 2 * step + tt;
+    if (j >= ntiles) return;
+    const int t0 = t_lo + kTile * j;
     const int nvalid = min(kTile, t_hi - t0);     // >= 1
-    // pages of the two 16-key halves (a 16-key half never crosses a page)
+    LDS_AS char* dst = tile_buf(step, tt) + 1024 * 9 * hb;
     const PageRef p0 = resolve_token(lt, slt, a.max_pages, b, (uint32_t)t0, (uint32_t)a.page_size);
     const uint8_t* rb0 = layer_base + (size_t)p0.page * (size_t)a.page_stride + (size_t)p0.slot * kHeadDim;
     const float* sb0 = slayer_base + (size_t)p0.spage * (size_t)a.spage_stride + (size_t)p0.slot * NG;
@@ -250,65 +255,58 @@ mla_decode_kernel(DecodeArgs a) {
       rb1 = layer_base + (size_t)p1.page * (size_t)a.page_stride + (size_t)p1.slot * kHeadDim;
       sb1 = slayer_base + (size_t)p1.spage * (size_t)a.spage_stride + (size_t)p1.slot * NG;
     }
-    LDS_AS char* dst = wbase + buf * kTileBytes;
     if (nvalid == kTile) {
+      const uint8_t* src = (hb ? rb1 : rb0) + ld_key * kHeadDim + 16 * ld_col;
 #pragma unroll
-      for (int i = 0; i < 18; ++i) {
-        const uint8_t* src = (i < 9 ? rb0 : rb1) + 64 * (i % 9) + ld_off;
-        lds_dma16(src, dst + 1024 * i);
-      }
+      for (int cb = 0; cb < 9; ++cb) lds_dma16(src + 64 * cb, dst + 1024 * cb);
     } else {
-      const int kmax0 = min(nvalid, 16) - 1;
-      const uint32_t off0 = (uint32_t)min(ld_key, kmax0) * kHeadDim + 16u * ld_col;
-      const uint8_t* base1 = nvalid > 16 ? rb1 : rb0 + kmax0 * kHeadDim;
-      const uint32_t off1 = (uint32_t)min(ld_key, max(nvalid - 17, 0)) * kHeadDim + 16u * ld_col;
+      const int kk = min(16 * hb + ld_key, nvalid - 1);
+      const uint8_t* src = (kk < 16 ? rb0 : rb1) + (kk & 15) * kHeadDim + 16 * ld_col;
 #pragma unroll
-      for (int i = 0; i < 18; ++i) {
-        const uint8_t* src = (i < 9 ? rb0 + off0 : base1 + off1) + 64 * (i % 9);
-        lds_dma16(src, dst + 1024 * i);
-      }
+      for (int cb = 0; cb < 9; ++cb) lds_dma16(src + 64 * cb, dst + 1024 * cb);
     }
-    LDS_AS char* sdst = wbase + 2 * kTileBytes + buf * LY::kScaleBytes;
-    const int key = min(lane & 31, nvalid - 1);
-    const float* srow = (key < 16 ? sb0 : sb1) + (key & 15) * NG;
-    if constexpr (NG == 1) {
-      lds_dma4(srow, sdst);
-    } else {
+    if (hb == 0) {
+      LDS_AS char* sdst = scale_buf(step, tt);
+      const int key = min(lane & 31, nvalid - 1);
+      const float* srow = (key < 16 ? sb0 : sb1) + (key & 15) * NG;
+      if constexpr (NG == 1) {
+        lds_dma4(srow, sdst);
+      } else {
+        // [group][key] layout: lane covers group 2i + lane/32 for key lane%32
 #pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const int grp = min(2 * i + (lane >> 5), NG - 1);
-        lds_dma4(srow + grp, sdst + 256 * i);
+        for (int i = 0; i < 5; ++i) lds_dma4(srow + min(2 * i + (lane >> 5), NG - 1), sdst + 256 * i);
       }
     }
   };
 
-  // ---- running state
-  f32x16 o[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = f32x16{};
-  // Reference max per row (S^T layout: lane column n; same value in both halves).
-  // It is fixed from the wave's first tile and never moved inside the loop, so
-  // the accumulators O are never rescaled: P' = f16(2^(x - m_ref) * scale) may
-  // exceed 1, which costs no precision in f16; only its overflow matters, and
-  // that case is caught after the pass (see the key loop).
-  float m_ref = kNegInf;
-  float l_part = 0.0f;       // this lane's share of the row sum (keys of its half)
+  if (nsteps > 0) issue_step(0);
 
-  const int ntiles = (t_hi - t_lo + kTile - 1) / kTile;
-  const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-  const int t_first = t_lo + kTile * wave;
+  const bool is_score = wave < 2;
+  // ================================================================ score waves
+  // per-lane row bookkeeping (S^T layout: lane column n is row rg*32 + n)
+  const int my_row = rg * kRows + n;
+  const bool row_ok = my_row < rows_total;
+  const int my_i = row_ok ? my_row / a.num_heads : 0;
+  // keys visible to this row: j < L - Q + i + 1, clipped to this split
+  const int lim = row_ok ? min(L - a.q_len + my_i + 1, t_hi) : t_hi;
+  int lim_min = row_ok ? lim : 0x7fffffff;
+  for (int off = 16; off >= 1; off >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
+  lim_min = __builtin_amdgcn_readfirstlane(min(lim_min, __shfl_xor(lim_min, 32)));
 
-  // Per-key scales of the keys this lane holds in the S^T layout (NG == 1).
-  auto key_scales = [&](LDS_AS const char* sb, float (&sv16)[16]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const f32x4 sv = *(LDS_AS const f32x4*)((LDS_AS const float*)sb + 8 * qq + 4 * g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sv16[4 * qq + e] = sv[e];
-    }
-  };
-  // Scales of group gv ([group][key] layout) for the keys this lane holds (NG == 9).
-  auto group_scales = [&](LDS_AS const char* sb, int gv, float (&sv16)[16]) __attribute__((always_inline)) {
+  // K read (A operand of the 32x32x64 MFMA): lane (key n, half g) reads 16-byte
+  // columns 4s + g and 4s + 2 + g of its key for 64-deep step s.
+  const uint32_t kread0 = (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((0 + g) ^ ((n >> 2) & 3))));
+  const uint32_t kread1 = (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((2 + g) ^ ((n >> 2) & 3))));
+  // V read (B operand via transpose read): provider lane p = 2k + h of each 16-lane
+  // group addresses key tau(g,k) = 4g + (k&3) + 8(k>>2) at column 32nb + 16q + 8h.
+  const int vq = (lane >> 4) & 1, vk = (lane & 15) >> 1, vh = lane & 1;
+  const int vtau = 4 * g + (vk & 3) + 8 * (vk >> 2);
+  const uint32_t vread0 = (uint32_t)(16 * (4 * vtau + ((0 + vq) ^ ((vtau >> 2) & 3))) + 8 * vh);
+  const uint32_t vread1 = (uint32_t)(16 * (4 * vtau + ((2 + vq) ^ ((vtau >> 2) & 3))) + 8 * vh);
+
+  // Scales of the 16 keys a lane holds in the S^T layout: per-key (NG == 1) or
+  // of group gv ([group][key] layout, NG == 9).
+  auto lane_scales = [&](LDS_AS const char* sb, int gv, float (&sv16)[16]) __attribute__((always_inline)) {
     LDS_AS const float* sg = (LDS_AS const float*)sb + 32 * gv;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
@@ -317,92 +315,206 @@ mla_decode_kernel(DecodeArgs a) {
       for (int e = 0; e < 4; ++e) sv16[4 * qq + e] = sv[e];
     }
   };
-  // Scores of one tile in the log2 domain (masked keys = -inf) and their row max.
-  auto tile_scores = [&](LDS_AS const char* tb, LDS_AS const char* sb, int t0, float (&x)[16])
-      __attribute__((always_inline)) -> float {
-    f32x16 s = f32x16{};
-    if constexpr (NG == 1) {
-#pragma unroll
-      for (int u = 0; u < 18; ++u) {
-        const u32x4 kr = *(LDS_AS const u32x4*)(tb + kread[u & 1] + 1024 * (u >> 1));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(fp8x8_to_f16(kr[0], kr[1]), qf[2 * u], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(fp8x8_to_f16(kr[2], kr[3]), qf[2 * u + 1], s, 0, 0, 0);
-        if (u & 1) sched_fence();
-      }
-      float sv16[16];
-      key_scales(sb, sv16);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (s[r] * sv16[r]) * a.sm_log2;
-    } else {
-      // one 64-deep scale group = 16-byte columns 4gi..4gi+3 = u in {2gi, 2gi+1}
-#pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        f32x16 t = f32x16{};
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-          const int u = 2 * gi + uu;
-          const u32x4 kr = *(LDS_AS const u32x4*)(tb + kread[u & 1] + 1024 * (u >> 1));
-          t = __builtin_amdgcn_mfma_f32_32x32x16_f16(fp8x8_to_f16(kr[0], kr[1]), qf[2 * u], t, 0, 0, 0);
-          t = __builtin_amdgcn_mfma_f32_32x32x16_f16(fp8x8_to_f16(kr[2], kr[3]), qf[2 * u + 1], t, 0, 0, 0);
+
+  // One tile of a score wave: S^T, masked base-2 scores, online softmax, and
+  // the hand-off of P' (NG == 1) or p (NG == 9) and the rescale factors.
+  // ================================================================ the step loops
+  // Each role runs its own copy of the step loop (so that the register
+  // allocator never sees q and the accumulators live together); both copies
+  // pass the same number of workgroup barriers.
+  LDS_AS float* const st = (LDS_AS float*)(L0 + LY::kStats);   // [m0, m1, l0, l1][32]
+  if (is_score) {
+    float m_run = kNegInf;     // score waves: running max per row (same in both halves)
+    float l_part = 0.0f;       // score waves: this lane's share of the row sum
+
+    // q of row n in the B-operand order of the 32x32x16 MFMAs: for 64-deep step
+    // st the four MFMAs take depths 64st + 16g + [0,8), + [8,16), 64st + 32 +
+    // 16g + [0,8), + [8,16) -- the same permutation of the depth index as the
+    // key bytes each lane reads (any common permutation leaves the sum alone).
+    bf16x8 qv[36];
+    {
+      const uint16_t* qrow = a.q + ((size_t)b * rows_total + (row_ok ? my_row : 0)) * kHeadDim;
+  #pragma unroll
+      for (int st = 0; st < 9; ++st) {
+  #pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const u32x4* src = (const u32x4*)(qrow + 64 * st + 32 * hf + 16 * g);
+          u32x4 w0 = src[0], w1 = src[1];
+          if (!row_ok) { w0 = u32x4{0, 0, 0, 0}; w1 = u32x4{0, 0, 0, 0}; }
+          qv[4 * st + 2 * hf] = __builtin_bit_cast(bf16x8, w0);
+          qv[4 * st + 2 * hf + 1] = __builtin_bit_cast(bf16x8, w1);
         }
-        float sv16[16];
-        group_scales(sb, gi, sv16);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(sv16[r], t[r], s[r]);
-        sched_fence();
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = s[r] * a.sm_log2;
     }
-    if (t0 + kTile > lim_min) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (t0 + tile_key(r, g) < lim) ? x[r] : kNegInf;
-    }
-    float mt = x[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
-    sched_fence();
-    return halves_max(mt);
-  };
-
-  // Probabilities, row sums, and O += P' V for one tile (P' = f16(p * scale)).
-  auto finish_tile = [&](LDS_AS const char* tb, LDS_AS const char* sb, const float (&x)[16])
-      __attribute__((always_inline)) {
-    const float m_use = m_ref == kNegInf ? 0.0f : m_ref;
-    float p[16];
-    float psum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = exp2_fast(x[r] - m_use);
-      psum += p[r];
-    }
-    l_part += psum;
-
-    if constexpr (NG == 1) {
+    wait_vmcnt<0>();            // tile 0 (every wave's share) and q have landed
+    __syncthreads();
+    auto score_tile = [&](int t0, LDS_AS const char* tb, LDS_AS const char* sb, LDS_AS char* pb,
+                          LDS_AS float* ab, LDS_AS const float* pm, bool has_pm) __attribute__((always_inline)) {
+      f32x16 s = f32x16{};
+  #pragma unroll
+      for (int st = 0; st < 9; ++st) {
+        const u32x4 k0 = *(LDS_AS const u32x4*)(tb + kread0 + 1024 * st);
+        const u32x4 k1 = *(LDS_AS const u32x4*)(tb + kread1 + 1024 * st);
+        f32x16 t = f32x16{};
+        f32x16& acc = NG == 1 ? s : t;
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k0[0], k0[1]), qv[4 * st + 0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k0[2], k0[3]), qv[4 * st + 1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k1[0], k1[1]), qv[4 * st + 2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k1[2], k1[3]), qv[4 * st + 3], acc, 0, 0, 0);
+        if constexpr (NG != 1) {
+          // 64-deep step st is scale group st: s += scale * (its partial sums)
+          float sv16[16];
+          lane_scales(sb, st, sv16);
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(sv16[r], t[r], s[r]);
+        }
+      }
+      float x[16];
       float sv16[16];
-      key_scales(sb, sv16);
+      if constexpr (NG == 1) {
+        lane_scales(sb, 0, sv16);
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (s[r] * sv16[r]) * a.sm_log2;
+      } else {
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = s[r] * a.sm_log2;
+      }
+      if (t0 + kTile > lim_min) {
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (t0 + tile_key(r, g) < lim) ? x[r] : kNegInf;
+      }
+      float mt = x[0];
+  #pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
+      mt = halves_max(mt);
+      // The reference max moves up to the partner score wave's (as it stood
+      // after the partner's previous tile), and lazily to this tile's max, only
+      // when a score here passes the reference by more than 8 (so p <= 2^8).
+      float mref = m_run;
+      if (has_pm) mref = fmaxf(mref, pm[n]);
+      if (wave_any(mt > mref + 8.0f)) mref = fmaxf(mref, mt);
+      if (wave_any(mref != m_run)) {
+        l_part *= m_run == kNegInf ? 0.0f : exp2_fast(m_run - mref);
+        m_run = mref;
+      }
+      ab[n] = m_run;                // the tile's reference; both halves write the same value
+      const float m_use = m_run == kNegInf ? 0.0f : m_run;
+      float p[16];
+      float psum = 0.0f;
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = exp2_fast(x[r] - m_use);
+        psum += p[r];
+      }
+      l_part += psum;
+      if constexpr (NG == 1) {
+        // P' = f16(p * key scale) in the A-operand order of the PV MFMA
+  #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          f16x8 pa;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) pa[e] = (_Float16)(p[8 * hh + e] * sv16[8 * hh + e]);
+          *(LDS_AS f16x8*)(pb + 1024 * hh + 16 * lane) = pa;
+        }
+      } else {
+  #pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          *(LDS_AS f32x4*)(pb + 1024 * qq + 16 * lane) = f32x4{p[4 * qq], p[4 * qq + 1], p[4 * qq + 2], p[4 * qq + 3]};
+      }
+    };
+
+    for (int i = 0; i <= nsteps; ++i) {
+      if (i + 1 < nsteps) issue_step(i + 1);
+      const int j = 2 * i + wave;
+      if (i < nsteps && j < ntiles)
+        score_tile(t_lo + kTile * j, tile_buf(i, wave), scale_buf(i, wave), p_buf(i, wave), alpha_buf(i, wave),
+                   alpha_buf(i + 1, wave ^ 1), i > 0);
+      wait_vmcnt<0>();          // this wave's loads of step i + 1 have landed
+      __syncthreads();
+    }
+    const float l_row = halves_sum(l_part);
+    if (g == 0) {
+      st[wave * kRows + n] = m_run;
+      st[(2 + wave) * kRows + n] = l_row;
+    }
+    __syncthreads();
+    return;
+  }
+
+  const int vc = wave & 1;            // value wave V_vc owns columns [256 vc, 256 vc + 256)
+  // O holds sum_j 2^(x_j - mO) s_j v_j for the row's reference max mO, kept per
+  // row in LDS (C-layout rows 8(r/4) + 4g + r%4) and in a register for the
+  // lane's A-layout row n.
+  LDS_AS float* const mo_lds = (LDS_AS float*)(L0 + LY::kMO) + kRows * vc;
+  float mo_a = kNegInf;
+  if (g == 0) mo_lds[n] = kNegInf;
+  f32x16 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x16{};
+  wait_vmcnt<0>();              // tile 0 (every wave's share) has landed
+  __syncthreads();
+  // One score wave's tile: bring O and the tile's P' to a common reference
+  // (rare: only when a reference moved), then O += P' V.
+  auto value_tile = [&](LDS_AS const char* tb, LDS_AS const char* sb, LDS_AS const char* pb,
+                        LDS_AS const float* ab) __attribute__((always_inline)) {
+    const float mt = ab[n];
+    float pf = 1.0f;
+    bool scale_p = false;
+    if (wave_any(mt != mo_a)) {
+      const float m_new = fmaxf(mo_a, mt);
+      if (wave_any(m_new != mo_a)) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const f32x4 old = *(LDS_AS const f32x4*)(mo_lds + 8 * qq + 4 * g);
+          const f32x4 tm = *(LDS_AS const f32x4*)(ab + 8 * qq + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float al = old[e] == kNegInf ? 0.0f : exp2_fast(old[e] - fmaxf(old[e], tm[e]));
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) o[nb][4 * qq + e] *= al;
+          }
+        }
+        if (g == 0) mo_lds[n] = m_new;
+      }
+      pf = mt == kNegInf ? 0.0f : exp2_fast(mt - m_new);
+      scale_p = wave_any(pf != 1.0f);
+      mo_a = m_new;
+    }
+    if constexpr (NG == 1) {
       f16x8 pa[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh) pa[hh] = *(LDS_AS const f16x8*)(pb + 1024 * hh + 16 * lane);
+      if (scale_p) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pa[hh][e] = (_Float16)(p[8 * hh + e] * sv16[8 * hh + e]);
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pa[hh][e] = (_Float16)((float)pa[hh][e] * pf);
+      }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-        for (int nb = 0; nb < 16; ++nb) {
+        for (int nl = 0; nl < 8; ++nl) {
+          const int nb = 8 * vc + nl;
           const i32x2 vr = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (LDS_AS i32x2*)(tb + vread[nb & 1] + 1024 * (9 * hh + (nb >> 1))));
-          o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              pa[hh], fp8x8_to_f16((uint32_t)vr[0], (uint32_t)vr[1]), o[nb], 0, 0, 0);
-          if ((nb & 3) == 3) sched_fence();
+              (LDS_AS i32x2*)(tb + ((nb & 1) ? vread1 : vread0) + 1024 * (9 * hh + (nb >> 1))));
+          o[nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              pa[hh], fp8x8_to_f16((uint32_t)vr[0], (uint32_t)vr[1]), o[nl], 0, 0, 0);
         }
       }
     } else {
-      // value group gv = columns [64gv, 64gv + 64) = output blocks nb = 2gv, 2gv+1
+      float p[16];
 #pragma unroll
-      for (int gv = 0; gv < 8; ++gv) {
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x4 pv = *(LDS_AS const f32x4*)(pb + 1024 * qq + 16 * lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[4 * qq + e] = pv[e] * pf;
+      }
+      // value group gv = columns [64gv, 64gv + 64) = blocks nb = 2gv, 2gv + 1
+#pragma unroll
+      for (int gl = 0; gl < 4; ++gl) {
+        const int gv = 4 * vc + gl;
         float sv16[16];
-        group_scales(sb, gv, sv16);
+        lane_scales(sb, gv, sv16);
         f16x8 pa[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -414,211 +526,73 @@ mla_decode_kernel(DecodeArgs a) {
           for (int nn = 0; nn < 2; ++nn) {
             const int nb = 2 * gv + nn;
             const i32x2 vr = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (LDS_AS i32x2*)(tb + vread[nb & 1] + 1024 * (9 * hh + (nb >> 1))));
-            o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                pa[hh], fp8x8_to_f16((uint32_t)vr[0], (uint32_t)vr[1]), o[nb], 0, 0, 0);
+                (LDS_AS i32x2*)(tb + ((nb & 1) ? vread1 : vread0) + 1024 * (9 * hh + (nb >> 1))));
+            o[2 * gl + nn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                pa[hh], fp8x8_to_f16((uint32_t)vr[0], (uint32_t)vr[1]), o[2 * gl + nn], 0, 0, 0);
           }
         }
-        sched_fence();
       }
     }
   };
 
-  // ---- the key loop.  Tile k of this wave starts at t_first + 128k; tile k+1's
-  // loads are in flight while tile k is computed.  Tiles run in chunks of
-  // kChunk against a reference max that is fixed inside a chunk (no VALU
-  // touches O in the tile loop); between chunks, if the running max moved, O
-  // and the row sums are rescaled once.  P' <= 2^(m_seen - m_ref) * (largest
-  // scale loaded); if that bound passes 2^15 within a chunk, the wave repeats
-  // its keys once from zero against the exact max, which it keeps tracking.
-  constexpr int kChunk = 4;
-  LDS_AS float* const alpha_buf = (LDS_AS float*)(wbase + 2 * kTileBytes + 2 * LY::kScaleBytes);
-  float m_all = kNegInf;       // running max over every tile seen (exact at the end)
-  for (int pass = 0; pass < 2; ++pass) {
-    bool overflow = false;
-    if (my_tiles > 0) issue_tile(t_first, 0);
-    for (int c0 = 0; c0 < my_tiles; c0 += kChunk) {
-      const int c1 = min(my_tiles, c0 + kChunk);
-      float m_seen = kNegInf;
-      float s_seen = 0.0f;     // largest scale this lane loaded in the chunk (its DMA slots)
-      for (int k = c0; k < c1; ++k) {
-        const int buf = k & 1;
-        const int t0 = t_first + kTile * kWaves * k;
-        if (k + 1 < my_tiles) {
-          issue_tile(t0 + kTile * kWaves, buf ^ 1);
-          if constexpr (NG == 1) wait_vmcnt<19>();   // this tile's loads; the next tile's stay in flight
-          else wait_vmcnt<23>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        LDS_AS const char* tb = wbase + buf * kTileBytes;
-        LDS_AS const char* sb = wbase + 2 * kTileBytes + buf * LY::kScaleBytes;
-
-        float x[16];
-        const float mt = tile_scores(tb, sb, t0, x);
-        m_seen = fmaxf(m_seen, mt);
-        if (k == 0 && pass == 0) m_ref = mt;
-        LDS_AS const float* sf = (LDS_AS const float*)sb;
-        s_seen = fmaxf(s_seen, sf[lane]);
-        if constexpr (NG == 9) {
-#pragma unroll
-          for (int i = 1; i < 5; ++i) s_seen = fmaxf(s_seen, sf[64 * i + lane]);
-        }
-        finish_tile(tb, sb, x);
-      }
-      m_all = fmaxf(m_all, m_seen);
-      if (pass == 0) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) s_seen = fmaxf(s_seen, __shfl_xor(s_seen, off));
-        const bool risky = m_seen != kNegInf && (m_seen - m_ref) + __log2f(s_seen) > 15.0f;
-        if (wave_any(risky)) {
-          overflow = true;
-          // finish the remaining scores only to learn the exact max
-          wait_vmcnt<0>();
-          for (int j = c1; j < my_tiles; ++j) {
-            const int tj = t_first + kTile * kWaves * j;
-            issue_tile(tj, 0);
-            wait_vmcnt<0>();
-            float xj[16];
-            m_all = fmaxf(m_all, tile_scores(wbase, wbase + 2 * kTileBytes, tj, xj));
-          }
-          break;
-        }
-      }
-      if (c1 < my_tiles && wave_any(m_seen > m_ref)) {
-        // move the reference to the running max: O and l scale by 2^(m_ref - m_new)
-        const float m_new = fmaxf(m_ref, m_seen);
-        const float alpha = m_ref == kNegInf ? 0.0f : exp2_fast(m_ref - m_new);
-        l_part *= alpha;
-        m_ref = m_new;
-        alpha_buf[n] = alpha;      // both halves hold the same value for row n
-        wait_lgkmcnt0();
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const f32x4 av = *(LDS_AS const f32x4*)(alpha_buf + 8 * qq + 4 * g);
-#pragma unroll
-          for (int nb = 0; nb < 16; ++nb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[nb][4 * qq + e] *= av[e];
-        }
-      }
+  for (int i = 0; i <= nsteps; ++i) {
+    if (i + 1 < nsteps) issue_step(i + 1);
+    if (i >= 1) {
+      value_tile(tile_buf(i - 1, 0), scale_buf(i - 1, 0), p_buf(i - 1, 0), alpha_buf(i - 1, 0));
+      if (2 * (i - 1) + 1 < ntiles)
+        value_tile(tile_buf(i - 1, 1), scale_buf(i - 1, 1), p_buf(i - 1, 1), alpha_buf(i - 1, 1));
     }
-    if (!overflow) break;
-    m_ref = m_all;
-    l_part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[i] = f32x16{};
+    wait_vmcnt<0>();          // this wave's loads of step i + 1 have landed
+    __syncthreads();
   }
+  __syncthreads();             // the score waves' (m, l) are in st
 
-  // ================================================================ merge the 4 waves
-  const float l_row = halves_sum(l_part);
-
-  __syncthreads();    // every wave is done with its tiles; LDS is free
-  LDS_AS float* const st_m = (LDS_AS float*)lds0;     // [4][32] running max per wave and row
-  LDS_AS float* const st_l = st_m + kWaves * kRows;   // [4][32] row sum per wave and row
-  if (g == 0) {
-    st_m[wave * kRows + n] = m_ref;
-    st_l[wave * kRows + n] = l_row;
-  }
-  __syncthreads();
-
-  // Scale this wave's O rows (PV layout: row 8(r/4) + 4g + r%4) by
-  // 2^(m_w - M) / L_total so that the 4 waves' O sum to the result.
+  // O / (2^(m0 - mO) l0 + 2^(m1 - mO) l1) per row, mO >= m0, m1
+  float lse_n = kNegInf;       // log2-sum-exp of row n (lanes g == 0)
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
-    f32x4 mw[kWaves], lw[kWaves];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      mw[w] = *(LDS_AS const f32x4*)(st_m + w * kRows + 8 * qq + 4 * g);
-      lw[w] = *(LDS_AS const f32x4*)(st_l + w * kRows + 8 * qq + 4 * g);
-    }
+    const f32x4 m0 = *(LDS_AS const f32x4*)(st + 0 * kRows + 8 * qq + 4 * g);
+    const f32x4 m1 = *(LDS_AS const f32x4*)(st + 1 * kRows + 8 * qq + 4 * g);
+    const f32x4 l0 = *(LDS_AS const f32x4*)(st + 2 * kRows + 8 * qq + 4 * g);
+    const f32x4 l1 = *(LDS_AS const f32x4*)(st + 3 * kRows + 8 * qq + 4 * g);
+    const f32x4 mo = *(LDS_AS const f32x4*)(mo_lds + 8 * qq + 4 * g);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float M = mw[0][e];
+      const float Lt = (m0[e] == kNegInf ? 0.0f : exp2_fast(m0[e] - mo[e]) * l0[e]) +
+                       (m1[e] == kNegInf ? 0.0f : exp2_fast(m1[e] - mo[e]) * l1[e]);
+      const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[w][e]);
-      float Lt = 0.0f, fself = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = mw[w][e] == kNegInf ? 0.0f : exp2_fast(mw[w][e] - M);
-        Lt += f * lw[w][e];
-        fself = w == wave ? f : fself;
-      }
-      const float fo = Lt > 0.0f ? fself / Lt : 0.0f;
-#pragma unroll
-      for (int nb = 0; nb < 16; ++nb) o[nb][4 * qq + e] *= fo;
+      for (int nb = 0; nb < 8; ++nb) o[nb][4 * qq + e] *= inv;
     }
   }
-  // the row's log2-sum-exp (S^T layout row n) for split partials
-  float lse_row = kNegInf;
-  {
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st_m[w * kRows + n]);
-    float Lt = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = st_m[w * kRows + n];
-      Lt += mw == kNegInf ? 0.0f : exp2_fast(mw - M) * st_l[w * kRows + n];
-    }
-    lse_row = Lt > 0.0f ? M + __log2f(Lt) : kNegInf;
+  if (g == 0) {
+    const float m0 = st[n], m1 = st[kRows + n], mo = mo_lds[n];
+    const float Lt = (m0 == kNegInf ? 0.0f : exp2_fast(m0 - mo) * st[2 * kRows + n]) +
+                     (m1 == kNegInf ? 0.0f : exp2_fast(m1 - mo) * st[3 * kRows + n]);
+    lse_n = Lt > 0.0f ? mo + __log2f(Lt) : kNegInf;
   }
-
-  // tree sum through LDS: [nb][r][lane] fp32 images, 64 KiB per wave
-  LDS_AS float* const red0 = (LDS_AS float*)(lds0 + 1024);
-  LDS_AS float* const red1 = red0 + 16 * 16 * 64;
-  auto put = [&](LDS_AS float* dst, int nb_lo, int nb_hi) __attribute__((always_inline)) {
-#pragma unroll
-    for (int nb = 0; nb < 16; ++nb)
-      if (nb >= nb_lo && nb < nb_hi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dst[(nb * 16 + r) * 64 + lane] = o[nb][r];
-  };
-  auto add = [&](LDS_AS const float* src, int nb_lo, int nb_hi) __attribute__((always_inline)) {
-#pragma unroll
-    for (int nb = 0; nb < 16; ++nb)
-      if (nb >= nb_lo && nb < nb_hi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[nb][r] += src[(nb * 16 + r) * 64 + lane];
-  };
-  __syncthreads();
-  if (wave == 2) put(red0, 0, 16);
-  if (wave == 3) put(red1, 0, 16);
-  __syncthreads();
-  if (wave == 0) add(red0, 0, 16);
-  if (wave == 1) add(red1, 0, 16);
-  __syncthreads();
-  if (wave == 0) put(red0, 8, 16);
-  if (wave == 1) put(red1, 0, 8);
-  __syncthreads();
-  if (wave == 0) add(red1, 0, 8);
-  if (wave == 1) add(red0, 8, 16);
-  if (wave >= 2) return;
-  const int nb_lo = wave == 0 ? 0 : 8;
 
   if (nsplit_eff == 1) {
-    // final rows: out[b, i, h, 32nb + n]
+    // final rows: out[b, i, h, 256 vc + 32 nb + n]
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = rg * kRows + tile_key(r, g);
       if (row < rows_total) {
-        uint16_t* orow = a.out + ((size_t)b * rows_total + row) * kVDim;
+        uint16_t* orow = a.out + ((size_t)b * rows_total + row) * kVDim + 256 * vc;
 #pragma unroll
-        for (int nb = 0; nb < 16; ++nb)
-          if (nb >= nb_lo && nb < nb_lo + 8) orow[32 * nb + n] = f32_to_bf16_bits(o[nb][r]);
+        for (int nb = 0; nb < 8; ++nb) orow[32 * nb + n] = f32_to_bf16_bits(o[nb][r]);
       }
     }
   } else {
     const size_t pidx = ((size_t)b * a.row_groups + rg) * a.num_splits + split;
-    float* po = a.ws_o + pidx * kRows * kVDim;
+    float* po = a.ws_o + pidx * kRows * kVDim + 256 * vc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float* prow = po + tile_key(r, g) * kVDim;
 #pragma unroll
-      for (int nb = 0; nb < 16; ++nb)
-        if (nb >= nb_lo && nb < nb_lo + 8) prow[32 * nb + n] = o[nb][r];
+      for (int nb = 0; nb < 8; ++nb) prow[32 * nb + n] = o[nb][r];
     }
-    if (wave == 0 && g == 0) a.ws_lse[pidx * kRows + n] = lse_row;
+    if (vc == 0 && g == 0) a.ws_lse[pidx * kRows + n] = lse_n;
   }
 }
 

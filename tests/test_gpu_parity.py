@@ -135,20 +135,25 @@ def test_shared_table_equals_independent_copy(gpu_device):
     assert torch.equal(out1, out2)
 
 
-def test_reference_max_too_low_redo(gpu_device):
-    """First tiles nearly zero, later keys huge: P' against the first tile's max
-    would overflow f16, so the waves repeat their keys against the exact max."""
-    say("overflow redo path")
-    w = _w(gpu_device, 2, 128, [1500, 700], 64, 576, seed=91, poison=True)
-    lt = w.lookup_table.to(torch.int64).cpu()
+@pytest.mark.parametrize("gran", [576, 64])
+def test_reference_max_jumps(gpu_device, gran):
+    """The first 128 keys (the first tiles of both score waves) score near zero,
+    later keys score far higher (q scaled by 8): each score wave's reference
+    max jumps mid-range, the partner follows it, and the value waves rescale
+    their accumulators and the P' tiles that were made against an older
+    reference.  Key scales stay in the workload's range (scaling them up would
+    inflate |V| far beyond |O|, where no f16 P' meets the gate)."""
+    say("reference max jumps", gran)
+    w = _w(gpu_device, 2, 128, [1500, 700], 64, gran, independent_scales=gran == 64,
+           spare_scale_blocks=2, seed=91, poison=True)
+    lt = (w.lookup_table.to(torch.int64) & 0xFFFFFFFF).cpu()
+    slt = lt if w.scales_lookup_table is None else (w.scales_lookup_table.to(torch.int64) & 0xFFFFFFFF).cpu()
     P = w.page_size
     for b, L in enumerate(w.lengths()):
-        for t in range(L):
-            page, slot = int(lt[b, t // P]), t % P
-            # keys 0..127 (first tiles of all four waves of split 0) tiny, others large
-            f = 1e-3 if t < 128 else 40.0
-            w.scales[page, 0, 0, slot, 0, :] *= f
+        for t in range(min(L, 128)):
+            w.scales[int(slt[b, t // P]), 0, 0, t % P, 0, :] *= 1e-3
+    w.q.mul_(8.0)
     torch.cuda.synchronize()
     ref = oracle_decode(w)
-    check_gate(run_gpu(w, num_splits=1), ref, "redo")
-    check_gate(run_gpu(w), ref, "redo, auto plan")
+    check_gate(run_gpu(w, num_splits=1), ref, "jump, one split")
+    check_gate(run_gpu(w), ref, "jump, auto plan")
