@@ -33,6 +33,10 @@ def hipcc_path() -> str:
 def device_flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in ordinary VGPRs: the online softmax rescales
+            # them with VALU ops, and AGPR accumulators would be copied to VGPRs
+            # and back on every loop iteration
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 

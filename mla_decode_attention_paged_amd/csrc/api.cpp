@@ -48,23 +48,25 @@ mla_status check_shape(const mla_shape* s, int32_t q_len) {
   return MLA_OK;
 }
 
-// Split plan.  Work units are (request, row group, key split); the number of
-// splits is the smallest that gives about one workgroup per compute unit,
-// capped so that each split keeps at least one 128-key chunk per wave, and
-// limited by the workspace the caller provided.
+// Split plan.  Work units are (request, pair of row groups, key split); the number of
+// splits is the smallest that gives about one workgroup per compute unit and
+// keeps every split within kMaxSplitKeys, capped so that each split keeps at
+// least one 128-key chunk, and limited by the workspace the caller provided.
 mla_status make_plan(const mla_shape* s, int32_t q_len, int32_t want_splits, size_t ws_limit,
                      bool ws_limited, mla_plan* p) {
   const int64_t rows = (int64_t)q_len * s->num_q_heads;
   const int64_t rg = (rows + kRows - 1) / kRows;
   const int64_t max_keys = (int64_t)s->max_pages * s->page_size;
   const int64_t chunks = (max_keys + kSplitQuantum - 1) / kSplitQuantum;
-  const int64_t units = (int64_t)s->batch * rg;
+  const int64_t units = (int64_t)s->batch * ((rg + 1) / 2);   // one workgroup per row-group pair
   int64_t splits;
   if (want_splits > 0) {
     splits = want_splits < chunks ? want_splits : chunks;
   } else {
     const int64_t target = device_cu_count();
     splits = units >= target ? 1 : (target + units - 1) / units;
+    const int64_t min_splits = (max_keys + mla::kMaxSplitKeys - 1) / mla::kMaxSplitKeys;
+    if (splits < min_splits) splits = min_splits;
     if (splits > chunks) splits = chunks;
     if (ws_limited) {
       while (splits > 1 && mla::partial_bytes(s->batch, rg, splits) > ws_limit) --splits;
@@ -135,7 +137,7 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
   a.row_groups = plan.row_groups;
   a.num_splits = plan.num_splits;
   a.tokens_per_split = plan.tokens_per_split;
-  a.grid_units = (int32_t)units;
+  a.grid_units = (int32_t)((size_t)shape->batch * ((plan.row_groups + 1) / 2) * plan.num_splits);
   a.sm_log2 = softmax_scale * 1.4426950408889634f;
 
   hipError_t e = mla::launch_decode(a, shape->scale_groups, stream, main_begin, main_end);

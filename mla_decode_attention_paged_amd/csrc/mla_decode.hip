@@ -127,6 +127,11 @@ __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcn
 __device__ __forceinline__ void lds_dma16(const void* gsrc, LDS_AS void* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
 }
+// Same, with an immediate offset added to both the global and the LDS address.
+template <int kOff>
+__device__ __forceinline__ void lds_dma16_off(const void* gsrc, LDS_AS void* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, kOff, 0);
+}
 __device__ __forceinline__ void lds_dma4(const void* gsrc, LDS_AS void* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, ldst, 4, 0, 0);
 }
@@ -137,44 +142,54 @@ __device__ __forceinline__ constexpr int tile_key(int r, int g) { return 8 * (r 
 
 // ---------------------------------------------------------------- the decode kernel
 //
-// Workgroup = 4 waves on one group of 32 query rows (q position, head) and one
-// key range [t_lo, t_hi) of one request.  The key range is cut into 32-key
-// tiles; a "step" is two consecutive tiles.  Roles:
+// Workgroup = 8 waves on a pair of 32-row groups (64 query rows: q position x
+// head) and one key range [t_lo, t_hi) of one request.  The key range is cut
+// into 32-key tiles; a "step" is two consecutive tiles, loaded once into LDS
+// and used by both row groups.  Roles (wave w runs on SIMD w % 4, so every
+// SIMD hosts one score and one value wave and overlaps one's VALU work with
+// the other's MFMAs):
 //
-//   score waves S0, S1 (waves 0, 1): S_w owns tile 2i + w of step i.  It holds
-//     q (bf16) for all 32 rows in registers, computes S^T = K Q^T on
+//   score waves (w = 0..3; row group r = w / 2, tile parity t = w % 2): own
+//     tile 2i + t of step i for the 32 rows of group r.  Each holds q (bf16)
+//     of its rows in registers, computes S^T = K Q^T on
 //     v_mfma_f32_32x32x16_bf16 with the keys widened FP8 -> bf16 as they come
-//     out of LDS, applies the key scales in fp32, runs the
-//     online softmax (its own row sums against a reference max that follows
-//     the partner score wave's and moves lazily), and hands P' (f16) and the
-//     tile's reference max per row to the value waves via LDS.
-//   value waves V0, V1 (waves 2, 3): V_c owns output columns [256c, 256c+256)
-//     and one accumulator O, and computes O += P' V on
-//     v_mfma_f32_32x32x16_f16 for both tiles of a step, one step behind the
-//     score waves, with V read from the same LDS tile through
-//     ds_read_b64_tr_b8.  When a tile's reference differs from O's, the
-//     smaller side is scaled to the larger (rare: references move lazily).
+//     out of LDS, applies the key scales in fp32, runs the online softmax
+//     (its own row sums against a reference max that follows the partner
+//     score wave's and moves lazily), and hands P' (f16) and the tile's
+//     reference max per row to the value waves via LDS.
+//   value waves (w = 4..7; row group r = (w - 4) / 2, column half c = w % 2):
+//     own output columns [256c, 256c + 256) of group r in one accumulator O
+//     and compute O += P' V on v_mfma_f32_32x32x16_f16 for both tiles of a
+//     step, one step behind the score waves, with V read from the same LDS
+//     tile through ds_read_b64_tr_b8.  When a tile's reference differs from
+//     O's, the smaller side is scaled to the larger (rare: references move
+//     lazily).  The value waves also issue the tile loads, one step ahead.
 //
-// Tiles arrive by direct global->LDS dwordx4 loads that all four waves issue
-// one step ahead; a tile buffer lives three steps (loaded, scored, consumed),
-// and one workgroup barrier per step orders the hand-offs.
+// Tiles arrive by direct global->LDS dwordx4 loads; a tile buffer lives three
+// steps (loaded, scored, consumed), and one workgroup barrier per step orders
+// the hand-offs.
+constexpr int kWaveCount = 8;
+constexpr int kThreads = 64 * kWaveCount;
+
 template <int NG>
 struct Layout {
   static constexpr int kScaleBytes = NG == 1 ? 256 : 1280;      // per tile
-  static constexpr int kPBytes = NG == 1 ? 2048 : 4096;         // P' (f16) or p (fp32) per tile
-  static constexpr int kTiles = 0;                               // 3 steps x 2 tiles
-  static constexpr int kScales = kTiles + 6 * kTileBytes;
-  static constexpr int kP = kScales + 6 * kScaleBytes;           // 2 steps x 2 tiles
-  static constexpr int kAlpha = kP + 4 * kPBytes;                // 2 steps x 2 tiles x 32 row maxima
-  static constexpr int kAlphaBytes = 128;
-  static constexpr int kStats = kAlpha + 4 * kAlphaBytes;        // m, l of both score waves
-  static constexpr int kMO = kStats + 4 * kRows * 4;             // reference max of each value wave's O
-  static constexpr int kTotal = kMO + 2 * kRows * 4;
+  static constexpr int kPBytes = NG == 1 ? 2048 : 4096;         // P' (f16) or p (fp32) per tile and group
+  static constexpr int kSlots = 3;                               // steps of tiles live at once
+  static constexpr int kTiles = 0;                               // kSlots steps x 2 tiles
+  static constexpr int kScales = kTiles + 2 * kSlots * kTileBytes;
+  static constexpr int kP = kScales + 2 * kSlots * kScaleBytes;  // [step % 2][tile][row group]
+  static constexpr int kAlphaBytes = 128;                        // 32 row maxima
+  static constexpr int kAlpha = kP + 8 * kPBytes;                // [step % 2][tile][row group]
+  static constexpr int kStats = kAlpha + 8 * kAlphaBytes;        // [row group][m0, m1, l0, l1][32]
+  static constexpr int kMO = kStats + 2 * 4 * kRows * 4;         // [value wave][32]: O's reference max
+  static constexpr int kPT = kMO + 4 * kRows * 4;                // value / scale page of each 16-key block
+  static constexpr int kTotal = kPT + 2 * kMaxBlocks16 * 4;
 };
-static_assert(Layout<9>::kTotal <= 160 * 1024, "LDS budget");
+static_assert(Layout<1>::kTotal <= 160 * 1024 && Layout<9>::kTotal <= 160 * 1024, "LDS budget");
 
 template <int NG>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 mla_decode_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   using LY = Layout<NG>;
@@ -183,18 +198,23 @@ mla_decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const bool is_score = wave < 4;
+  const int sub = wave & 3;
+  const int rgl = sub >> 1;         // row group within the pair
   const int g = lane >> 5;          // lane half
   const int n = lane & 31;          // MFMA column / row within the half
 
-  // ---- XCD-aware unit mapping: consecutive units (the row groups of one key
-  // range) land on the same XCD and are dispatched back to back there.
+  // ---- XCD-aware unit mapping: consecutive units (the row-group pairs of one
+  // key range, which read the same keys) land on the same XCD back to back.
+  const int rgp_count = (a.row_groups + 1) >> 1;
   const int per_xcd = (a.grid_units + 7) >> 3;
   const int unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (unit >= a.grid_units) return;
-  const int rg = unit % a.row_groups;
-  const int bs = unit / a.row_groups;
+  const int rgp = unit % rgp_count;
+  const int bs = unit / rgp_count;
   const int split = bs % a.num_splits;
   const int b = bs / a.num_splits;
+  const int rg = 2 * rgp + rgl;     // this wave's row group (>= row_groups: no valid rows)
 
   const CONST_AS uint32_t* const lt = (const CONST_AS uint32_t*)a.lt;
   const CONST_AS uint32_t* const slt = (const CONST_AS uint32_t*)a.slt;
@@ -209,20 +229,22 @@ mla_decode_kernel(DecodeArgs a) {
   const int ntiles = (t_hi - t_lo + kTile - 1) / kTile;
   const int nsteps = (ntiles + 1) / 2;
   const int rows_total = a.q_len * a.num_heads;
+  const float c2 = a.sm_log2;                  // scores are kept unscaled; exponents are c2 * (x - m)
 
   // ---- LDS regions
   auto tile_buf = [&](int step, int tt) __attribute__((always_inline)) {
-    return L0 + LY::kTiles + ((step % 3) * 2 + tt) * kTileBytes;
+    return L0 + LY::kTiles + ((step % LY::kSlots) * 2 + tt) * kTileBytes;
   };
   auto scale_buf = [&](int step, int tt) __attribute__((always_inline)) {
-    return L0 + LY::kScales + ((step % 3) * 2 + tt) * LY::kScaleBytes;
+    return L0 + LY::kScales + ((step % LY::kSlots) * 2 + tt) * LY::kScaleBytes;
   };
-  auto p_buf = [&](int step, int tt) __attribute__((always_inline)) {
-    return L0 + LY::kP + ((step & 1) * 2 + tt) * LY::kPBytes;
+  auto p_buf = [&](int step, int tt, int r) __attribute__((always_inline)) {
+    return L0 + LY::kP + (((step & 1) * 2 + tt) * 2 + r) * LY::kPBytes;
   };
-  auto alpha_buf = [&](int step, int tt) __attribute__((always_inline)) {
-    return (LDS_AS float*)(L0 + LY::kAlpha + ((step & 1) * 2 + tt) * LY::kAlphaBytes);
+  auto alpha_buf = [&](int step, int tt, int r) __attribute__((always_inline)) {
+    return (LDS_AS float*)(L0 + LY::kAlpha + (((step & 1) * 2 + tt) * 2 + r) * LY::kAlphaBytes);
   };
+  LDS_AS float* const st = (LDS_AS float*)(L0 + LY::kStats) + rgl * 4 * kRows;   // [m0, m1, l0, l1][32]
 
   // ---- tile loads.  Global->LDS tile layout: 18 blocks of 1 KiB, block
   // 9*(key/16) + col/64; inside a block, 16-byte slot 4*(key%16) +
@@ -233,42 +255,70 @@ mla_decode_kernel(DecodeArgs a) {
   const uint8_t* layer_base = a.blocks + a.layer_offset;
   const float* slayer_base = a.scales + a.slayer_offset;
 
-  // Wave w loads half (w & 1) of tile (w >> 1) of `step` (9 blocks), and the
-  // scales of that tile when it loads half 0.  Keys at or past t_hi are never
-  // read: their lanes re-load the last valid key (finite data that the softmax
-  // masks out), so slots, pages and table columns past a request's length stay
-  // untouched.
+  // The pages of the key range, one value page and one scale page per 16-key
+  // block (a block never straddles a page: pages hold a multiple of 16 keys),
+  // are copied into LDS once, so that the per-step address math reads LDS
+  // rather than waiting on scalar loads of the page tables.  Blocks past the
+  // first kMaxBlocks16 (splits longer than the plan makes them) read the
+  // tables directly.
+  LDS_AS uint32_t* const pt = (LDS_AS uint32_t*)(L0 + LY::kPT);
+  LDS_AS uint32_t* const spt = pt + kMaxBlocks16;
+  auto copy_pages = [&]() __attribute__((always_inline)) {
+    const int nblk = min((t_hi - t_lo + 15) >> 4, kMaxBlocks16);
+    const uint32_t* ltr = a.lt + (size_t)b * a.max_pages;
+    const uint32_t* sltr = a.slt + (size_t)b * a.max_pages;
+    for (int u = tid; u < nblk; u += kThreads) {
+      const uint32_t col = (uint32_t)(t_lo + 16 * u) / (uint32_t)a.page_size;
+      pt[u] = ltr[col];
+      spt[u] = sltr[col];
+    }
+  };
+  auto block_page = [&](int blk, bool scale) __attribute__((always_inline)) -> uint32_t {
+    if (blk < kMaxBlocks16) return __builtin_amdgcn_readfirstlane(scale ? spt[blk] : pt[blk]);
+    const uint32_t col = (uint32_t)(t_lo + 16 * blk) / (uint32_t)a.page_size;
+    return (scale ? slt : lt)[(size_t)b * a.max_pages + col];
+  };
+
+  // Value wave sub loads half (sub & 1) of tile (sub >> 1) of `step` (9
+  // blocks), and the scales of that tile when it loads half 0.  Keys at or past
+  // t_hi are never read: their lanes re-load the last valid key (finite data
+  // that the softmax masks out), so slots, pages and table columns past a
+  // request's length stay untouched.
   auto issue_step = [&](int step) __attribute__((always_inline)) {
-    const int tt = wave >> 1, hb = wave & 1;
+    const int tt = sub >> 1, hb = sub & 1;
     const int j = 2 * step + tt;
     if (j >= ntiles) return;
     const int t0 = t_lo + kTile * j;
     const int nvalid = min(kTile, t_hi - t0);     // >= 1
+    const int blk0 = (t0 - t_lo) >> 4;
     LDS_AS char* dst = tile_buf(step, tt) + 1024 * 9 * hb;
-    const PageRef p0 = resolve_token(lt, slt, a.max_pages, b, (uint32_t)t0, (uint32_t)a.page_size);
-    const uint8_t* rb0 = layer_base + (size_t)p0.page * (size_t)a.page_stride + (size_t)p0.slot * kHeadDim;
-    const float* sb0 = slayer_base + (size_t)p0.spage * (size_t)a.spage_stride + (size_t)p0.slot * NG;
-    const uint8_t* rb1 = rb0;
-    const float* sb1 = sb0;
-    if (nvalid > 16) {
-      const PageRef p1 = resolve_token(lt, slt, a.max_pages, b, (uint32_t)(t0 + 16), (uint32_t)a.page_size);
-      rb1 = layer_base + (size_t)p1.page * (size_t)a.page_stride + (size_t)p1.slot * kHeadDim;
-      sb1 = slayer_base + (size_t)p1.spage * (size_t)a.spage_stride + (size_t)p1.slot * NG;
-    }
-    if (nvalid == kTile) {
-      const uint8_t* src = (hb ? rb1 : rb0) + ld_key * kHeadDim + 16 * ld_col;
-#pragma unroll
-      for (int cb = 0; cb < 9; ++cb) lds_dma16(src + 64 * cb, dst + 1024 * cb);
-    } else {
+    // slots of the tile's two 16-key halves (the second only if it exists)
+    const uint32_t slot0 = (uint32_t)t0 % (uint32_t)a.page_size;
+    const uint32_t slot1 = nvalid > 16 ? (uint32_t)(t0 + 16) % (uint32_t)a.page_size : slot0;
+    const int bh = nvalid > 16 ? 1 : 0;           // block of the second half (clamped)
+    {
       const int kk = min(16 * hb + ld_key, nvalid - 1);
-      const uint8_t* src = (kk < 16 ? rb0 : rb1) + (kk & 15) * kHeadDim + 16 * ld_col;
-#pragma unroll
-      for (int cb = 0; cb < 9; ++cb) lds_dma16(src + 64 * cb, dst + 1024 * cb);
+      const int half = __builtin_amdgcn_readfirstlane(min(hb, bh));   // half holding this wave's keys
+      const uint32_t page = block_page(blk0 + half, false);
+      const uint32_t slot = half ? slot1 : slot0;
+      const uint8_t* src = layer_base + (size_t)page * (size_t)a.page_stride +
+                           (size_t)(slot + (uint32_t)(kk - 16 * half)) * kHeadDim + 16 * ld_col;
+      // The nine loads share one address register: column block cb sits 64 B
+      // further in HBM, given by the instruction's immediate offset.  That
+      // offset also moves the LDS address, so the LDS base steps by 1024 - 64.
+#define MLA_DMA_CB(cb) lds_dma16_off<64 * (cb)>(src, dst + (1024 - 64) * (cb))
+      MLA_DMA_CB(0); MLA_DMA_CB(1); MLA_DMA_CB(2); MLA_DMA_CB(3); MLA_DMA_CB(4);
+      MLA_DMA_CB(5); MLA_DMA_CB(6); MLA_DMA_CB(7); MLA_DMA_CB(8);
+#undef MLA_DMA_CB
     }
     if (hb == 0) {
       LDS_AS char* sdst = scale_buf(step, tt);
       const int key = min(lane & 31, nvalid - 1);
-      const float* srow = (key < 16 ? sb0 : sb1) + (key & 15) * NG;
+      const int kh = key >> 4;
+      const uint32_t sp0 = block_page(blk0, true);
+      const uint32_t sp1 = block_page(blk0 + bh, true);
+      const float* srow = slayer_base + (size_t)(kh ? sp1 : sp0) * (size_t)a.spage_stride +
+                          (size_t)((kh ? slot1 : slot0) + (uint32_t)(key & 15)) * NG;
       if constexpr (NG == 1) {
         lds_dma4(srow, sdst);
       } else {
@@ -279,30 +329,9 @@ mla_decode_kernel(DecodeArgs a) {
     }
   };
 
-  if (nsteps > 0) issue_step(0);
-
-  const bool is_score = wave < 2;
-  // ================================================================ score waves
   // per-lane row bookkeeping (S^T layout: lane column n is row rg*32 + n)
   const int my_row = rg * kRows + n;
   const bool row_ok = my_row < rows_total;
-  const int my_i = row_ok ? my_row / a.num_heads : 0;
-  // keys visible to this row: j < L - Q + i + 1, clipped to this split
-  const int lim = row_ok ? min(L - a.q_len + my_i + 1, t_hi) : t_hi;
-  int lim_min = row_ok ? lim : 0x7fffffff;
-  for (int off = 16; off >= 1; off >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
-  lim_min = __builtin_amdgcn_readfirstlane(min(lim_min, __shfl_xor(lim_min, 32)));
-
-  // K read (A operand of the 32x32x64 MFMA): lane (key n, half g) reads 16-byte
-  // columns 4s + g and 4s + 2 + g of its key for 64-deep step s.
-  const uint32_t kread0 = (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((0 + g) ^ ((n >> 2) & 3))));
-  const uint32_t kread1 = (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((2 + g) ^ ((n >> 2) & 3))));
-  // V read (B operand via transpose read): provider lane p = 2k + h of each 16-lane
-  // group addresses key tau(g,k) = 4g + (k&3) + 8(k>>2) at column 32nb + 16q + 8h.
-  const int vq = (lane >> 4) & 1, vk = (lane & 15) >> 1, vh = lane & 1;
-  const int vtau = 4 * g + (vk & 3) + 8 * (vk >> 2);
-  const uint32_t vread0 = (uint32_t)(16 * (4 * vtau + ((0 + vq) ^ ((vtau >> 2) & 3))) + 8 * vh);
-  const uint32_t vread1 = (uint32_t)(16 * (4 * vtau + ((2 + vq) ^ ((vtau >> 2) & 3))) + 8 * vh);
 
   // Scales of the 16 keys a lane holds in the S^T layout: per-key (NG == 1) or
   // of group gv ([group][key] layout, NG == 9).
@@ -316,16 +345,27 @@ mla_decode_kernel(DecodeArgs a) {
     }
   };
 
-  // One tile of a score wave: S^T, masked base-2 scores, online softmax, and
-  // the hand-off of P' (NG == 1) or p (NG == 9) and the rescale factors.
   // ================================================================ the step loops
   // Each role runs its own copy of the step loop (so that the register
   // allocator never sees q and the accumulators live together); both copies
   // pass the same number of workgroup barriers.
-  LDS_AS float* const st = (LDS_AS float*)(L0 + LY::kStats);   // [m0, m1, l0, l1][32]
   if (is_score) {
-    float m_run = kNegInf;     // score waves: running max per row (same in both halves)
-    float l_part = 0.0f;       // score waves: this lane's share of the row sum
+    const int par = sub & 1;   // tile parity this wave scores
+    const int my_i = row_ok ? my_row / a.num_heads : 0;
+    // keys visible to this row: j < L - Q + i + 1, clipped to this split
+    const int lim = row_ok ? min(L - a.q_len + my_i + 1, t_hi) : t_hi;
+    int lim_min = row_ok ? lim : 0x7fffffff;
+    for (int off = 16; off >= 1; off >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
+    lim_min = __builtin_amdgcn_readfirstlane(min(lim_min, __shfl_xor(lim_min, 32)));
+    // K read (A operand): lane (key n, half g) reads 16-byte columns 4s + g and
+    // 4s + 2 + g of its key for 64-deep step s.
+    const uint32_t kread0 = (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((0 + g) ^ ((n >> 2) & 3))));
+    const uint32_t kread1 = (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((2 + g) ^ ((n >> 2) & 3))));
+    // lazy threshold: the reference moves when a score passes it by 8 / c2 (p <= 2^8)
+    const float thr = 8.0f / c2;
+
+    float m_run = kNegInf;     // running reference max per row (same in both halves), unscaled
+    float l_part = 0.0f;       // this lane's share of the row sum, against m_run
 
     // q of row n in the B-operand order of the 32x32x16 MFMAs: for 64-deep step
     // st the four MFMAs take depths 64st + 16g + [0,8), + [8,16), 64st + 32 +
@@ -335,49 +375,57 @@ mla_decode_kernel(DecodeArgs a) {
     {
       const uint16_t* qrow = a.q + ((size_t)b * rows_total + (row_ok ? my_row : 0)) * kHeadDim;
   #pragma unroll
-      for (int st = 0; st < 9; ++st) {
+      for (int s = 0; s < 9; ++s) {
   #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const u32x4* src = (const u32x4*)(qrow + 64 * st + 32 * hf + 16 * g);
+          const u32x4* src = (const u32x4*)(qrow + 64 * s + 32 * hf + 16 * g);
           u32x4 w0 = src[0], w1 = src[1];
           if (!row_ok) { w0 = u32x4{0, 0, 0, 0}; w1 = u32x4{0, 0, 0, 0}; }
-          qv[4 * st + 2 * hf] = __builtin_bit_cast(bf16x8, w0);
-          qv[4 * st + 2 * hf + 1] = __builtin_bit_cast(bf16x8, w1);
+          qv[4 * s + 2 * hf] = __builtin_bit_cast(bf16x8, w0);
+          qv[4 * s + 2 * hf + 1] = __builtin_bit_cast(bf16x8, w1);
         }
       }
     }
-    wait_vmcnt<0>();            // tile 0 (every wave's share) and q have landed
-    __syncthreads();
+    copy_pages();
+    __syncthreads();            // the page copy is visible
+    wait_vmcnt<0>();            // q has landed
+    __syncthreads();            // step 0 has landed (the value waves waited for their loads)
+
     auto score_tile = [&](int t0, LDS_AS const char* tb, LDS_AS const char* sb, LDS_AS char* pb,
                           LDS_AS float* ab, LDS_AS const float* pm, bool has_pm) __attribute__((always_inline)) {
-      f32x16 s = f32x16{};
+      // Two accumulator banks take alternate MFMAs, so consecutive MFMAs never
+      // wait on each other's result (a 32x32x16 MFMA's latency is about two
+      // issue slots).
+      f32x16 s = f32x16{}, s1 = f32x16{};
   #pragma unroll
-      for (int st = 0; st < 9; ++st) {
-        const u32x4 k0 = *(LDS_AS const u32x4*)(tb + kread0 + 1024 * st);
-        const u32x4 k1 = *(LDS_AS const u32x4*)(tb + kread1 + 1024 * st);
-        f32x16 t = f32x16{};
-        f32x16& acc = NG == 1 ? s : t;
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k0[0], k0[1]), qv[4 * st + 0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k0[2], k0[3]), qv[4 * st + 1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k1[0], k1[1]), qv[4 * st + 2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k1[2], k1[3]), qv[4 * st + 3], acc, 0, 0, 0);
+      for (int ks = 0; ks < 9; ++ks) {
+        const u32x4 k0 = *(LDS_AS const u32x4*)(tb + kread0 + 1024 * ks);
+        const u32x4 k1 = *(LDS_AS const u32x4*)(tb + kread1 + 1024 * ks);
+        f32x16 t0 = f32x16{}, t1 = f32x16{};
+        f32x16& a0 = NG == 1 ? s : t0;
+        f32x16& a1 = NG == 1 ? s1 : t1;
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k0[0], k0[1]), qv[4 * ks + 0], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k0[2], k0[3]), qv[4 * ks + 1], a1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k1[0], k1[1]), qv[4 * ks + 2], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k1[2], k1[3]), qv[4 * ks + 3], a1, 0, 0, 0);
         if constexpr (NG != 1) {
-          // 64-deep step st is scale group st: s += scale * (its partial sums)
+          // 64-deep step ks is scale group ks: s += scale * (its partial sums)
           float sv16[16];
-          lane_scales(sb, st, sv16);
+          lane_scales(sb, ks, sv16);
   #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(sv16[r], t[r], s[r]);
+          for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(sv16[r], t0[r] + t1[r], s[r]);
         }
       }
+      // x = the scaled score without softmax_scale (exponents use c2 * (x - m))
       float x[16];
       float sv16[16];
       if constexpr (NG == 1) {
         lane_scales(sb, 0, sv16);
   #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (s[r] * sv16[r]) * a.sm_log2;
+        for (int r = 0; r < 16; ++r) x[r] = (s[r] + s1[r]) * sv16[r];
       } else {
   #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = s[r] * a.sm_log2;
+        for (int r = 0; r < 16; ++r) x[r] = s[r];
       }
       if (t0 + kTile > lim_min) {
   #pragma unroll
@@ -389,21 +437,21 @@ mla_decode_kernel(DecodeArgs a) {
       mt = halves_max(mt);
       // The reference max moves up to the partner score wave's (as it stood
       // after the partner's previous tile), and lazily to this tile's max, only
-      // when a score here passes the reference by more than 8 (so p <= 2^8).
+      // when a score here passes the reference by more than thr.
       float mref = m_run;
       if (has_pm) mref = fmaxf(mref, pm[n]);
-      if (wave_any(mt > mref + 8.0f)) mref = fmaxf(mref, mt);
+      if (wave_any(mt > mref + thr)) mref = fmaxf(mref, mt);
       if (wave_any(mref != m_run)) {
-        l_part *= m_run == kNegInf ? 0.0f : exp2_fast(m_run - mref);
+        l_part *= m_run == kNegInf ? 0.0f : exp2_fast((m_run - mref) * c2);
         m_run = mref;
       }
       ab[n] = m_run;                // the tile's reference; both halves write the same value
-      const float m_use = m_run == kNegInf ? 0.0f : m_run;
+      const float nm = m_run == kNegInf ? 0.0f : -m_run * c2;
       float p[16];
       float psum = 0.0f;
   #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = exp2_fast(x[r] - m_use);
+        p[r] = exp2_fast(__builtin_fmaf(x[r], c2, nm));
         psum += p[r];
       }
       l_part += psum;
@@ -424,40 +472,55 @@ mla_decode_kernel(DecodeArgs a) {
     };
 
     for (int i = 0; i <= nsteps; ++i) {
-      if (i + 1 < nsteps) issue_step(i + 1);
-      const int j = 2 * i + wave;
+      const int j = 2 * i + par;
       if (i < nsteps && j < ntiles)
-        score_tile(t_lo + kTile * j, tile_buf(i, wave), scale_buf(i, wave), p_buf(i, wave), alpha_buf(i, wave),
-                   alpha_buf(i + 1, wave ^ 1), i > 0);
-      wait_vmcnt<0>();          // this wave's loads of step i + 1 have landed
+        score_tile(t_lo + kTile * j, tile_buf(i, par), scale_buf(i, par), p_buf(i, par, rgl),
+                   alpha_buf(i, par, rgl), alpha_buf(i + 1, par ^ 1, rgl), i > 0);
       __syncthreads();
     }
     const float l_row = halves_sum(l_part);
     if (g == 0) {
-      st[wave * kRows + n] = m_run;
-      st[(2 + wave) * kRows + n] = l_row;
+      st[par * kRows + n] = m_run;
+      st[(2 + par) * kRows + n] = l_row;
     }
     __syncthreads();
     return;
   }
 
-  const int vc = wave & 1;            // value wave V_vc owns columns [256 vc, 256 vc + 256)
-  // O holds sum_j 2^(x_j - mO) s_j v_j for the row's reference max mO, kept per
-  // row in LDS (C-layout rows 8(r/4) + 4g + r%4) and in a register for the
-  // lane's A-layout row n.
-  LDS_AS float* const mo_lds = (LDS_AS float*)(L0 + LY::kMO) + kRows * vc;
+  // ================================================================ value waves
+  const int vc = sub & 1;             // value wave owns columns [256 vc, 256 vc + 256) of group rgl
+  // O holds sum_j 2^(c2 (x_j - mO)) s_j v_j for the row's reference max mO,
+  // kept per row in LDS (C-layout rows 8(r/4) + 4g + r%4) and in a register
+  // for the lane's A-layout row n.
+  LDS_AS float* const mo_lds = (LDS_AS float*)(L0 + LY::kMO) + kRows * sub;
   float mo_a = kNegInf;
   if (g == 0) mo_lds[n] = kNegInf;
+  // V read (B operand via transpose read): provider lane p = 2k + h of each 16-lane
+  // group addresses key tau(g,k) = 4g + (k&3) + 8(k>>2) at column 32nb + 16q + 8h.
+  const int vq = (lane >> 4) & 1, vk = (lane & 15) >> 1, vh = lane & 1;
+  const int vtau = 4 * g + (vk & 3) + 8 * (vk >> 2);
+  const uint32_t vread0 = (uint32_t)(16 * (4 * vtau + ((0 + vq) ^ ((vtau >> 2) & 3))) + 8 * vh);
+  const uint32_t vread1 = (uint32_t)(16 * (4 * vtau + ((2 + vq) ^ ((vtau >> 2) & 3))) + 8 * vh);
   f32x16 o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x16{};
-  wait_vmcnt<0>();              // tile 0 (every wave's share) has landed
+  copy_pages();
+  __syncthreads();              // the page copy is visible
+  if (nsteps > 0) issue_step(0);
+  wait_vmcnt<0>();              // this wave's share of step 0 has landed
   __syncthreads();
+
+  // P' (f16, NG == 1) or p (fp32, NG == 9) of one tile in this lane's A-operand
+  // order, as raw dwords read from LDS at the top of a step.
+  typedef u32x4 PRaw[NG == 1 ? 2 : 4];
+  auto load_p = [&](LDS_AS const char* pb, PRaw& pr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < (NG == 1 ? 2 : 4); ++k) pr[k] = *(LDS_AS const u32x4*)(pb + 1024 * k + 16 * lane);
+  };
   // One score wave's tile: bring O and the tile's P' to a common reference
   // (rare: only when a reference moved), then O += P' V.
-  auto value_tile = [&](LDS_AS const char* tb, LDS_AS const char* sb, LDS_AS const char* pb,
-                        LDS_AS const float* ab) __attribute__((always_inline)) {
-    const float mt = ab[n];
+  auto value_tile = [&](LDS_AS const char* tb, LDS_AS const char* sb, LDS_AS const float* ab, float mt,
+                        const PRaw& pr) __attribute__((always_inline)) {
     float pf = 1.0f;
     bool scale_p = false;
     if (wave_any(mt != mo_a)) {
@@ -469,21 +532,21 @@ mla_decode_kernel(DecodeArgs a) {
           const f32x4 tm = *(LDS_AS const f32x4*)(ab + 8 * qq + 4 * g);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float al = old[e] == kNegInf ? 0.0f : exp2_fast(old[e] - fmaxf(old[e], tm[e]));
+            const float al = old[e] == kNegInf ? 0.0f : exp2_fast((old[e] - fmaxf(old[e], tm[e])) * c2);
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) o[nb][4 * qq + e] *= al;
           }
         }
         if (g == 0) mo_lds[n] = m_new;
       }
-      pf = mt == kNegInf ? 0.0f : exp2_fast(mt - m_new);
+      pf = mt == kNegInf ? 0.0f : exp2_fast((mt - m_new) * c2);
       scale_p = wave_any(pf != 1.0f);
       mo_a = m_new;
     }
     if constexpr (NG == 1) {
       f16x8 pa[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) pa[hh] = *(LDS_AS const f16x8*)(pb + 1024 * hh + 16 * lane);
+      for (int hh = 0; hh < 2; ++hh) pa[hh] = __builtin_bit_cast(f16x8, pr[hh]);
       if (scale_p) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -505,7 +568,7 @@ mla_decode_kernel(DecodeArgs a) {
       float p[16];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const f32x4 pv = *(LDS_AS const f32x4*)(pb + 1024 * qq + 16 * lane);
+        const f32x4 pv = __builtin_bit_cast(f32x4, pr[qq]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[4 * qq + e] = pv[e] * pf;
       }
@@ -538,16 +601,22 @@ mla_decode_kernel(DecodeArgs a) {
   for (int i = 0; i <= nsteps; ++i) {
     if (i + 1 < nsteps) issue_step(i + 1);
     if (i >= 1) {
-      value_tile(tile_buf(i - 1, 0), scale_buf(i - 1, 0), p_buf(i - 1, 0), alpha_buf(i - 1, 0));
+      // both tiles' hand-offs are read up front, so their LDS latency is paid once
+      // (the second tile's buffers hold stale data when it does not exist)
+      PRaw p0, p1;
+      const float mt0 = alpha_buf(i - 1, 0, rgl)[n], mt1 = alpha_buf(i - 1, 1, rgl)[n];
+      load_p(p_buf(i - 1, 0, rgl), p0);
+      load_p(p_buf(i - 1, 1, rgl), p1);
+      value_tile(tile_buf(i - 1, 0), scale_buf(i - 1, 0), alpha_buf(i - 1, 0, rgl), mt0, p0);
       if (2 * (i - 1) + 1 < ntiles)
-        value_tile(tile_buf(i - 1, 1), scale_buf(i - 1, 1), p_buf(i - 1, 1), alpha_buf(i - 1, 1));
+        value_tile(tile_buf(i - 1, 1), scale_buf(i - 1, 1), alpha_buf(i - 1, 1, rgl), mt1, p1);
     }
     wait_vmcnt<0>();          // this wave's loads of step i + 1 have landed
     __syncthreads();
   }
   __syncthreads();             // the score waves' (m, l) are in st
 
-  // O / (2^(m0 - mO) l0 + 2^(m1 - mO) l1) per row, mO >= m0, m1
+  // O / (2^(c2 (m0 - mO)) l0 + 2^(c2 (m1 - mO)) l1) per row, mO >= m0, m1
   float lse_n = kNegInf;       // log2-sum-exp of row n (lanes g == 0)
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
@@ -558,8 +627,8 @@ mla_decode_kernel(DecodeArgs a) {
     const f32x4 mo = *(LDS_AS const f32x4*)(mo_lds + 8 * qq + 4 * g);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float Lt = (m0[e] == kNegInf ? 0.0f : exp2_fast(m0[e] - mo[e]) * l0[e]) +
-                       (m1[e] == kNegInf ? 0.0f : exp2_fast(m1[e] - mo[e]) * l1[e]);
+      const float Lt = (m0[e] == kNegInf ? 0.0f : exp2_fast((m0[e] - mo[e]) * c2) * l0[e]) +
+                       (m1[e] == kNegInf ? 0.0f : exp2_fast((m1[e] - mo[e]) * c2) * l1[e]);
       const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) o[nb][4 * qq + e] *= inv;
@@ -567,11 +636,12 @@ mla_decode_kernel(DecodeArgs a) {
   }
   if (g == 0) {
     const float m0 = st[n], m1 = st[kRows + n], mo = mo_lds[n];
-    const float Lt = (m0 == kNegInf ? 0.0f : exp2_fast(m0 - mo) * st[2 * kRows + n]) +
-                     (m1 == kNegInf ? 0.0f : exp2_fast(m1 - mo) * st[3 * kRows + n]);
-    lse_n = Lt > 0.0f ? mo + __log2f(Lt) : kNegInf;
+    const float Lt = (m0 == kNegInf ? 0.0f : exp2_fast((m0 - mo) * c2) * st[2 * kRows + n]) +
+                     (m1 == kNegInf ? 0.0f : exp2_fast((m1 - mo) * c2) * st[3 * kRows + n]);
+    lse_n = Lt > 0.0f ? mo * c2 + __log2f(Lt) : kNegInf;
   }
 
+  if (rg >= a.row_groups) return;    // the pair's second group does not exist
   if (nsplit_eff == 1) {
     // final rows: out[b, i, h, 256 vc + 32 nb + n]
 #pragma unroll
@@ -688,7 +758,7 @@ static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream) {
     attr_set = true;
   }
   const int per_xcd = (a.grid_units + 7) / 8;
-  hipLaunchKernelGGL(mla_decode_kernel<NG>, dim3(8 * per_xcd), dim3(256), lds_bytes, stream, a);
+  hipLaunchKernelGGL(mla_decode_kernel<NG>, dim3(8 * per_xcd), dim3(kThreads), lds_bytes, stream, a);
   return hipGetLastError();
 }
 

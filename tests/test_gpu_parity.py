@@ -109,6 +109,18 @@ def test_forced_splits(gpu_device, splits):
     check_gate(base, ref, "splits 1")
 
 
+def test_split_longer_than_the_page_copy(gpu_device):
+    """One split per request over up to 20000 keys with 16-key pages: the first
+    8192 keys' page ids come from the workgroup's LDS copy, the rest straight
+    from the tables."""
+    say("split longer than the LDS page copy")
+    w = _w(gpu_device, 2, 128, [9000, 20000], 16, 64, independent_scales=True, spare_blocks=3,
+           spare_scale_blocks=3, seed=77, poison=True, unused_table_id=0xFFFFFFFF)
+    ref = oracle_decode(w)
+    check_gate(run_gpu(w, num_splits=1), ref, "one split, 20000 keys")
+    check_gate(run_gpu(w), ref, "auto plan")
+
+
 # ------------------------------------------------------------------ invariances on the GPU
 def test_page_permutation_bitwise(gpu_device):
     say("permutation invariance")
