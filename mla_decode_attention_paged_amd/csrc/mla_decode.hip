@@ -145,29 +145,31 @@ __device__ __forceinline__ constexpr int tile_key(int r, int g) { return 8 * (r 
 // Workgroup = 8 waves on a pair of 32-row groups (64 query rows: q position x
 // head) and one key range [t_lo, t_hi) of one request.  The key range is cut
 // into 32-key tiles; a "step" is two consecutive tiles, loaded once into LDS
-// and used by both row groups.  Roles (wave w runs on SIMD w % 4, so every
-// SIMD hosts one score and one value wave and overlaps one's VALU work with
-// the other's MFMAs):
+// and used by both row groups.  Wave w runs on SIMD w % 4, so every SIMD
+// hosts one score and one value wave; their phases are arranged so that one
+// wave's VALU work (FP8 widening, softmax) overlaps the other's MFMAs.
 //
-//   score waves (w = 0..3; row group r = w / 2, tile parity t = w % 2): own
-//     tile 2i + t of step i for the 32 rows of group r.  Each holds q (bf16)
-//     of its rows in registers, computes S^T = K Q^T on
-//     v_mfma_f32_32x32x16_bf16 with the keys widened FP8 -> bf16 as they come
-//     out of LDS, applies the key scales in fp32, runs the online softmax
-//     (its own row sums against a reference max that follows the partner
-//     score wave's and moves lazily), and hands P' (f16) and the tile's
-//     reference max per row to the value waves via LDS.
-//   value waves (w = 4..7; row group r = (w - 4) / 2, column half c = w % 2):
-//     own output columns [256c, 256c + 256) of group r in one accumulator O
-//     and compute O += P' V on v_mfma_f32_32x32x16_f16 for both tiles of a
-//     step, one step behind the score waves, with V read from the same LDS
-//     tile through ds_read_b64_tr_b8.  When a tile's reference differs from
-//     O's, the smaller side is scaled to the larger (rare: references move
-//     lazily).  The value waves also issue the tile loads, one step ahead.
+//   score waves (w = 0..3; tile parity t = w / 2, depth half d = w % 2): for
+//     tile 2i + t of step i, compute the partial S^T = K Q^T of both row
+//     groups over their half of the 576-deep dot product (bytes [32d, 32d+32)
+//     of every 64-byte block), on v_mfma_f32_32x32x16_bf16 with q (bf16) in
+//     registers and the keys widened FP8 -> bf16 once for both groups.  The
+//     two halves of a tile swap partial sums through LDS at the mid-step
+//     barrier; then wave (t, d) finishes row group d: key scales (fp32),
+//     online softmax against a reference max that follows the other tile's
+//     wave and moves lazily, and the hand-off of P' (f16) and the tile's
+//     reference max to the value waves.
+//   value waves (w = 4..7; column quarter c = w - 4): own output columns
+//     [128c, 128c + 128) of both row groups and compute O += P' V on
+//     v_mfma_f32_32x32x16_f16 for the two tiles of the previous step (one
+//     before the mid-step barrier, one after), widening each V fragment once
+//     for both groups.  When a tile's reference differs from O's, the smaller
+//     side is scaled to the larger (rare: references move lazily).  The
+//     value waves also issue the tile loads, one step ahead.
 //
 // Tiles arrive by direct global->LDS dwordx4 loads; a tile buffer lives three
-// steps (loaded, scored, consumed), and one workgroup barrier per step orders
-// the hand-offs.
+// steps (loaded, scored, consumed).  Two workgroup barriers per step order the
+// hand-offs.
 constexpr int kWaveCount = 8;
 constexpr int kThreads = 64 * kWaveCount;
 
@@ -175,6 +177,7 @@ template <int NG>
 struct Layout {
   static constexpr int kScaleBytes = NG == 1 ? 256 : 1280;      // per tile
   static constexpr int kPBytes = NG == 1 ? 2048 : 4096;         // P' (f16) or p (fp32) per tile and group
+  static constexpr int kXBytes = 4096;                           // a 32 x 32 fp32 partial score tile
   static constexpr int kSlots = 3;                               // steps of tiles live at once
   static constexpr int kTiles = 0;                               // kSlots steps x 2 tiles
   static constexpr int kScales = kTiles + 2 * kSlots * kTileBytes;
@@ -182,9 +185,13 @@ struct Layout {
   static constexpr int kAlphaBytes = 128;                        // 32 row maxima
   static constexpr int kAlpha = kP + 8 * kPBytes;                // [step % 2][tile][row group]
   static constexpr int kStats = kAlpha + 8 * kAlphaBytes;        // [row group][m0, m1, l0, l1][32]
-  static constexpr int kMO = kStats + 2 * 4 * kRows * 4;         // [value wave][32]: O's reference max
-  static constexpr int kPT = kMO + 4 * kRows * 4;                // value / scale page of each 16-key block
-  static constexpr int kTotal = kPT + 2 * kMaxBlocks16 * 4;
+  static constexpr int kMO = kStats + 2 * 4 * kRows * 4;         // [value wave][row group][32]: O's reference
+  // partial-score exchange [tile][row group]: its own region when a P slot is
+  // smaller than a score tile, else the P slot of the step being scored (its
+  // owner reads the exchange before writing P' there)
+  static constexpr bool kXOwn = kPBytes < kXBytes;
+  static constexpr int kX = kMO + 8 * kRows * 4;
+  static constexpr int kTotal = kX + (kXOwn ? 4 * kXBytes : 0);
 };
 static_assert(Layout<1>::kTotal <= 160 * 1024 && Layout<9>::kTotal <= 160 * 1024, "LDS budget");
 
@@ -200,7 +207,6 @@ mla_decode_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const bool is_score = wave < 4;
   const int sub = wave & 3;
-  const int rgl = sub >> 1;         // row group within the pair
   const int g = lane >> 5;          // lane half
   const int n = lane & 31;          // MFMA column / row within the half
 
@@ -214,7 +220,6 @@ mla_decode_kernel(DecodeArgs a) {
   const int bs = unit / rgp_count;
   const int split = bs % a.num_splits;
   const int b = bs / a.num_splits;
-  const int rg = 2 * rgp + rgl;     // this wave's row group (>= row_groups: no valid rows)
 
   const CONST_AS uint32_t* const lt = (const CONST_AS uint32_t*)a.lt;
   const CONST_AS uint32_t* const slt = (const CONST_AS uint32_t*)a.slt;
@@ -244,7 +249,12 @@ mla_decode_kernel(DecodeArgs a) {
   auto alpha_buf = [&](int step, int tt, int r) __attribute__((always_inline)) {
     return (LDS_AS float*)(L0 + LY::kAlpha + (((step & 1) * 2 + tt) * 2 + r) * LY::kAlphaBytes);
   };
-  LDS_AS float* const st = (LDS_AS float*)(L0 + LY::kStats) + rgl * 4 * kRows;   // [m0, m1, l0, l1][32]
+  auto x_buf = [&](int step, int tt, int r) __attribute__((always_inline)) {
+    return LY::kXOwn ? L0 + LY::kX + (tt * 2 + r) * LY::kXBytes : p_buf(step, tt, r);
+  };
+  auto stats = [&](int r) __attribute__((always_inline)) {   // [m0, m1, l0, l1][32] of row group r
+    return (LDS_AS float*)(L0 + LY::kStats) + r * 4 * kRows;
+  };
 
   // ---- tile loads.  Global->LDS tile layout: 18 blocks of 1 KiB, block
   // 9*(key/16) + col/64; inside a block, 16-byte slot 4*(key%16) +
@@ -255,28 +265,37 @@ mla_decode_kernel(DecodeArgs a) {
   const uint8_t* layer_base = a.blocks + a.layer_offset;
   const float* slayer_base = a.scales + a.slayer_offset;
 
-  // The pages of the key range, one value page and one scale page per 16-key
-  // block (a block never straddles a page: pages hold a multiple of 16 keys),
-  // are copied into LDS once, so that the per-step address math reads LDS
-  // rather than waiting on scalar loads of the page tables.  Blocks past the
-  // first kMaxBlocks16 (splits longer than the plan makes them) read the
-  // tables directly.
-  LDS_AS uint32_t* const pt = (LDS_AS uint32_t*)(L0 + LY::kPT);
-  LDS_AS uint32_t* const spt = pt + kMaxBlocks16;
-  auto copy_pages = [&]() __attribute__((always_inline)) {
-    const int nblk = min((t_hi - t_lo + 15) >> 4, kMaxBlocks16);
-    const uint32_t* ltr = a.lt + (size_t)b * a.max_pages;
-    const uint32_t* sltr = a.slt + (size_t)b * a.max_pages;
-    for (int u = tid; u < nblk; u += kThreads) {
-      const uint32_t col = (uint32_t)(t_lo + 16 * u) / (uint32_t)a.page_size;
-      pt[u] = ltr[col];
-      spt[u] = sltr[col];
+  // Row offsets of the key range's 16-key blocks (a block never straddles a
+  // page: pages hold a multiple of 16 keys), 64 blocks (16 steps) at a time:
+  // lane k of the value waves holds the byte offset of block 64 m + k's first
+  // row in blocks[.., layer] and the float offset of its scale row, so that a
+  // step's addresses come from v_readlane rather than from memory.  The page
+  // ids of window m + 1 are prefetched while window m is in use.
+  const int nblk = (t_hi - t_lo + 15) >> 4;
+  const uint32_t* ltr = a.lt + (size_t)b * a.max_pages;
+  const uint32_t* sltr = a.slt + (size_t)b * a.max_pages;
+  uint32_t nxt_page = 0, nxt_spage = 0;          // raw page ids of the prefetched window
+  uint64_t w_off = 0, w_soff = 0;                // offsets of the current window
+  int cur_win = -1;
+  auto fetch_window = [&](int m) __attribute__((always_inline)) {
+    const int blk = 64 * m + lane;
+    if (blk < nblk) {
+      const uint32_t col = (uint32_t)(t_lo + 16 * blk) / (uint32_t)a.page_size;
+      nxt_page = ltr[col];
+      nxt_spage = sltr[col];
     }
   };
-  auto block_page = [&](int blk, bool scale) __attribute__((always_inline)) -> uint32_t {
-    if (blk < kMaxBlocks16) return __builtin_amdgcn_readfirstlane(scale ? spt[blk] : pt[blk]);
-    const uint32_t col = (uint32_t)(t_lo + 16 * blk) / (uint32_t)a.page_size;
-    return (scale ? slt : lt)[(size_t)b * a.max_pages + col];
+  auto enter_window = [&](int m) __attribute__((always_inline)) {
+    const uint32_t slot = (uint32_t)(t_lo + 16 * (64 * m + lane)) % (uint32_t)a.page_size;
+    w_off = (uint64_t)nxt_page * (uint64_t)a.page_stride + (uint64_t)slot * kHeadDim;
+    w_soff = (uint64_t)nxt_spage * (uint64_t)a.spage_stride + (uint64_t)slot * NG;
+    cur_win = m;
+    if (64 * (m + 1) < nblk) fetch_window(m + 1);
+  };
+  auto lane_u64 = [&](uint64_t v, int k) __attribute__((always_inline)) -> uint64_t {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, k);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), k);
+    return ((uint64_t)hi << 32) | lo;
   };
 
   // Value wave sub loads half (sub & 1) of tile (sub >> 1) of `step` (9
@@ -290,19 +309,15 @@ mla_decode_kernel(DecodeArgs a) {
     if (j >= ntiles) return;
     const int t0 = t_lo + kTile * j;
     const int nvalid = min(kTile, t_hi - t0);     // >= 1
-    const int blk0 = (t0 - t_lo) >> 4;
+    if ((step >> 4) != cur_win) enter_window(step >> 4);
+    const int blk0 = ((t0 - t_lo) >> 4) & 63;     // lane of the tile's first block in the window
     LDS_AS char* dst = tile_buf(step, tt) + 1024 * 9 * hb;
-    // slots of the tile's two 16-key halves (the second only if it exists)
-    const uint32_t slot0 = (uint32_t)t0 % (uint32_t)a.page_size;
-    const uint32_t slot1 = nvalid > 16 ? (uint32_t)(t0 + 16) % (uint32_t)a.page_size : slot0;
     const int bh = nvalid > 16 ? 1 : 0;           // block of the second half (clamped)
     {
       const int kk = min(16 * hb + ld_key, nvalid - 1);
       const int half = __builtin_amdgcn_readfirstlane(min(hb, bh));   // half holding this wave's keys
-      const uint32_t page = block_page(blk0 + half, false);
-      const uint32_t slot = half ? slot1 : slot0;
-      const uint8_t* src = layer_base + (size_t)page * (size_t)a.page_stride +
-                           (size_t)(slot + (uint32_t)(kk - 16 * half)) * kHeadDim + 16 * ld_col;
+      const uint8_t* src = layer_base + lane_u64(w_off, blk0 + half) +
+                           (size_t)(uint32_t)(kk - 16 * half) * kHeadDim + 16 * ld_col;
       // The nine loads share one address register: column block cb sits 64 B
       // further in HBM, given by the instruction's immediate offset.  That
       // offset also moves the LDS address, so the LDS base steps by 1024 - 64.
@@ -314,11 +329,8 @@ mla_decode_kernel(DecodeArgs a) {
     if (hb == 0) {
       LDS_AS char* sdst = scale_buf(step, tt);
       const int key = min(lane & 31, nvalid - 1);
-      const int kh = key >> 4;
-      const uint32_t sp0 = block_page(blk0, true);
-      const uint32_t sp1 = block_page(blk0 + bh, true);
-      const float* srow = slayer_base + (size_t)(kh ? sp1 : sp0) * (size_t)a.spage_stride +
-                          (size_t)((kh ? slot1 : slot0) + (uint32_t)(key & 15)) * NG;
+      const uint64_t so0 = lane_u64(w_soff, blk0), so1 = lane_u64(w_soff, blk0 + bh);
+      const float* srow = slayer_base + ((key >> 4) ? so1 : so0) + (size_t)(key & 15) * NG;
       if constexpr (NG == 1) {
         lds_dma4(srow, sdst);
       } else {
@@ -328,10 +340,6 @@ mla_decode_kernel(DecodeArgs a) {
       }
     }
   };
-
-  // per-lane row bookkeeping (S^T layout: lane column n is row rg*32 + n)
-  const int my_row = rg * kRows + n;
-  const bool row_ok = my_row < rows_total;
 
   // Scales of the 16 keys a lane holds in the S^T layout: per-key (NG == 1) or
   // of group gv ([group][key] layout, NG == 9).
@@ -350,136 +358,168 @@ mla_decode_kernel(DecodeArgs a) {
   // allocator never sees q and the accumulators live together); both copies
   // pass the same number of workgroup barriers.
   if (is_score) {
-    const int par = sub & 1;   // tile parity this wave scores
+    const int par = sub >> 1;      // tile parity this wave scores
+    const int d = sub & 1;         // depth half; also the row group it finishes
+    // rows of row group d (the softmax side) in the S^T layout: lane column n
+    const int my_row = (2 * rgp + d) * kRows + n;
+    const bool row_ok = my_row < rows_total;
     const int my_i = row_ok ? my_row / a.num_heads : 0;
     // keys visible to this row: j < L - Q + i + 1, clipped to this split
     const int lim = row_ok ? min(L - a.q_len + my_i + 1, t_hi) : t_hi;
     int lim_min = row_ok ? lim : 0x7fffffff;
     for (int off = 16; off >= 1; off >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
     lim_min = __builtin_amdgcn_readfirstlane(min(lim_min, __shfl_xor(lim_min, 32)));
-    // K read (A operand): lane (key n, half g) reads 16-byte columns 4s + g and
-    // 4s + 2 + g of its key for 64-deep step s.
-    const uint32_t kread0 = (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((0 + g) ^ ((n >> 2) & 3))));
-    const uint32_t kread1 = (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((2 + g) ^ ((n >> 2) & 3))));
+    // K read (A operand): lane (key n, half g) reads 16-byte column 4s + 2d + g
+    // of its key for 64-byte block s.
+    const uint32_t kread = (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((2 * d + g) ^ ((n >> 2) & 3))));
     // lazy threshold: the reference moves when a score passes it by 8 / c2 (p <= 2^8)
     const float thr = 8.0f / c2;
 
     float m_run = kNegInf;     // running reference max per row (same in both halves), unscaled
     float l_part = 0.0f;       // this lane's share of the row sum, against m_run
 
-    // q of row n in the B-operand order of the 32x32x16 MFMAs: for 64-deep step
-    // st the four MFMAs take depths 64st + 16g + [0,8), + [8,16), 64st + 32 +
-    // 16g + [0,8), + [8,16) -- the same permutation of the depth index as the
-    // key bytes each lane reads (any common permutation leaves the sum alone).
-    bf16x8 qv[36];
+    // q of both row groups in the B-operand order of the 32x32x16 MFMAs: for
+    // block s the two MFMAs take depths 64s + 32d + 16g + [0,8) and + [8,16) --
+    // the same depths as the key bytes each lane reads.
+    bf16x8 qv[2][18];
     {
-      const uint16_t* qrow = a.q + ((size_t)b * rows_total + (row_ok ? my_row : 0)) * kHeadDim;
-  #pragma unroll
-      for (int s = 0; s < 9; ++s) {
-  #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const u32x4* src = (const u32x4*)(qrow + 64 * s + 32 * hf + 16 * g);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = (2 * rgp + r) * kRows + n;
+        const bool ok = row < rows_total;
+        const uint16_t* qrow = a.q + ((size_t)b * rows_total + (ok ? row : 0)) * kHeadDim + 32 * d + 16 * g;
+#pragma unroll
+        for (int s = 0; s < 9; ++s) {
+          const u32x4* src = (const u32x4*)(qrow + 64 * s);
           u32x4 w0 = src[0], w1 = src[1];
-          if (!row_ok) { w0 = u32x4{0, 0, 0, 0}; w1 = u32x4{0, 0, 0, 0}; }
-          qv[4 * s + 2 * hf] = __builtin_bit_cast(bf16x8, w0);
-          qv[4 * s + 2 * hf + 1] = __builtin_bit_cast(bf16x8, w1);
+          if (!ok) { w0 = u32x4{0, 0, 0, 0}; w1 = u32x4{0, 0, 0, 0}; }
+          qv[r][2 * s] = __builtin_bit_cast(bf16x8, w0);
+          qv[r][2 * s + 1] = __builtin_bit_cast(bf16x8, w1);
         }
       }
     }
-    copy_pages();
-    __syncthreads();            // the page copy is visible
     wait_vmcnt<0>();            // q has landed
     __syncthreads();            // step 0 has landed (the value waves waited for their loads)
 
-    auto score_tile = [&](int t0, LDS_AS const char* tb, LDS_AS const char* sb, LDS_AS char* pb,
-                          LDS_AS float* ab, LDS_AS const float* pm, bool has_pm) __attribute__((always_inline)) {
-      // Two accumulator banks take alternate MFMAs, so consecutive MFMAs never
-      // wait on each other's result (a 32x32x16 MFMA's latency is about two
-      // issue slots).
-      f32x16 s = f32x16{}, s1 = f32x16{};
-  #pragma unroll
-      for (int ks = 0; ks < 9; ++ks) {
-        const u32x4 k0 = *(LDS_AS const u32x4*)(tb + kread0 + 1024 * ks);
-        const u32x4 k1 = *(LDS_AS const u32x4*)(tb + kread1 + 1024 * ks);
-        f32x16 t0 = f32x16{}, t1 = f32x16{};
-        f32x16& a0 = NG == 1 ? s : t0;
-        f32x16& a1 = NG == 1 ? s1 : t1;
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k0[0], k0[1]), qv[4 * ks + 0], a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k0[2], k0[3]), qv[4 * ks + 1], a1, 0, 0, 0);
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k1[0], k1[1]), qv[4 * ks + 2], a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(k1[2], k1[3]), qv[4 * ks + 3], a1, 0, 0, 0);
-        if constexpr (NG != 1) {
-          // 64-deep step ks is scale group ks: s += scale * (its partial sums)
-          float sv16[16];
-          lane_scales(sb, ks, sv16);
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(sv16[r], t0[r] + t1[r], s[r]);
-        }
-      }
-      // x = the scaled score without softmax_scale (exponents use c2 * (x - m))
-      float x[16];
-      float sv16[16];
-      if constexpr (NG == 1) {
-        lane_scales(sb, 0, sv16);
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (s[r] + s1[r]) * sv16[r];
-      } else {
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = s[r];
-      }
-      if (t0 + kTile > lim_min) {
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (t0 + tile_key(r, g) < lim) ? x[r] : kNegInf;
-      }
-      float mt = x[0];
-  #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
-      mt = halves_max(mt);
-      // The reference max moves up to the partner score wave's (as it stood
-      // after the partner's previous tile), and lazily to this tile's max, only
-      // when a score here passes the reference by more than thr.
-      float mref = m_run;
-      if (has_pm) mref = fmaxf(mref, pm[n]);
-      if (wave_any(mt > mref + thr)) mref = fmaxf(mref, mt);
-      if (wave_any(mref != m_run)) {
-        l_part *= m_run == kNegInf ? 0.0f : exp2_fast((m_run - mref) * c2);
-        m_run = mref;
-      }
-      ab[n] = m_run;                // the tile's reference; both halves write the same value
-      const float nm = m_run == kNegInf ? 0.0f : -m_run * c2;
-      float p[16];
-      float psum = 0.0f;
-  #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = exp2_fast(__builtin_fmaf(x[r], c2, nm));
-        psum += p[r];
-      }
-      l_part += psum;
-      if constexpr (NG == 1) {
-        // P' = f16(p * key scale) in the A-operand order of the PV MFMA
-  #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          f16x8 pa;
-  #pragma unroll
-          for (int e = 0; e < 8; ++e) pa[e] = (_Float16)(p[8 * hh + e] * sv16[8 * hh + e]);
-          *(LDS_AS f16x8*)(pb + 1024 * hh + 16 * lane) = pa;
-        }
-      } else {
-  #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          *(LDS_AS f32x4*)(pb + 1024 * qq + 16 * lane) = f32x4{p[4 * qq], p[4 * qq + 1], p[4 * qq + 2], p[4 * qq + 3]};
-      }
-    };
-
     for (int i = 0; i <= nsteps; ++i) {
       const int j = 2 * i + par;
-      if (i < nsteps && j < ntiles)
-        score_tile(t_lo + kTile * j, tile_buf(i, par), scale_buf(i, par), p_buf(i, par, rgl),
-                   alpha_buf(i, par, rgl), alpha_buf(i + 1, par ^ 1, rgl), i > 0);
-      __syncthreads();
+      const bool have = i < nsteps && j < ntiles;
+      const int t0 = t_lo + kTile * j;
+      LDS_AS const char* tb = tile_buf(i, par);
+      LDS_AS const char* sb = scale_buf(i, par);
+      // ---- phase 1: partial scores of both row groups over depth half d
+      f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+      if (have) {
+        // all nine key reads are issued up front: one LDS latency per tile (the
+        // group-scale variant, short of registers, reads them as it goes)
+        u32x4 kws[9];
+        if constexpr (NG == 1) {
+#pragma unroll
+          for (int s = 0; s < 9; ++s) kws[s] = *(LDS_AS const u32x4*)(tb + kread + 1024 * s);
+          sched_fence();
+        }
+#pragma unroll
+        for (int s = 0; s < 9; ++s) {
+          const u32x4 kw = NG == 1 ? kws[s] : *(LDS_AS const u32x4*)(tb + kread + 1024 * s);
+          const bf16x8 k0 = fp8x8_to_bf16(kw[0], kw[1]);
+          const bf16x8 k1 = fp8x8_to_bf16(kw[2], kw[3]);
+          if constexpr (NG == 1) {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv[0][2 * s], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv[1][2 * s], acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv[0][2 * s + 1], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv[1][2 * s + 1], acc1, 0, 0, 0);
+          } else {
+            // block s is scale group s: acc += scale * (this half's partial sums)
+            f32x16 u0 = f32x16{}, u1 = f32x16{};
+            u0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv[0][2 * s], u0, 0, 0, 0);
+            u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv[1][2 * s], u1, 0, 0, 0);
+            u0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv[0][2 * s + 1], u0, 0, 0, 0);
+            u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv[1][2 * s + 1], u1, 0, 0, 0);
+            float sv16[16];
+            lane_scales(sb, s, sv16);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              acc0[r] = __builtin_fmaf(sv16[r], u0[r], acc0[r]);
+              acc1[r] = __builtin_fmaf(sv16[r], u1[r], acc1[r]);
+            }
+          }
+        }
+        // the other row group's partial goes to the wave finishing it (same tile, depth 1 - d)
+        LDS_AS char* xo = x_buf(i, par, d ^ 1);
+        const f32x16& give = d ? acc0 : acc1;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          *(LDS_AS f32x4*)(xo + 1024 * qq + 16 * lane) = f32x4{give[4 * qq], give[4 * qq + 1], give[4 * qq + 2], give[4 * qq + 3]};
+      }
+      __syncthreads();          // mid-step: partial scores exchanged
+      // ---- phase 2: row group d of this tile: full scores, online softmax, P'
+      if (have) {
+        LDS_AS const char* xi = x_buf(i, par, d);
+        const f32x16& keep = d ? acc1 : acc0;
+        float x[16];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const f32x4 o4 = *(LDS_AS const f32x4*)(xi + 1024 * qq + 16 * lane);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * qq + e] = keep[4 * qq + e] + o4[e];
+        }
+        // x = the scaled score without softmax_scale (exponents use c2 * (x - m))
+        float sv16[16];
+        if constexpr (NG == 1) {
+          lane_scales(sb, 0, sv16);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[r] *= sv16[r];
+        }
+        if (t0 + kTile > lim_min) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[r] = (t0 + tile_key(r, g) < lim) ? x[r] : kNegInf;
+        }
+        float mt = x[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
+        mt = halves_max(mt);
+        // The reference max moves up to the other tile's wave's (as it stood
+        // after its previous tile), and lazily to this tile's max, only when a
+        // score here passes the reference by more than thr.
+        LDS_AS float* ab = alpha_buf(i, par, d);
+        float mref = m_run;
+        if (i > 0) mref = fmaxf(mref, alpha_buf(i - 1, par ^ 1, d)[n]);
+        if (wave_any(mt > mref + thr)) mref = fmaxf(mref, mt);
+        if (wave_any(mref != m_run)) {
+          l_part *= m_run == kNegInf ? 0.0f : exp2_fast((m_run - mref) * c2);
+          m_run = mref;
+        }
+        ab[n] = m_run;                // the tile's reference; both halves write the same value
+        const float nm = m_run == kNegInf ? 0.0f : -m_run * c2;
+        float p[16];
+        float psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = exp2_fast(__builtin_fmaf(x[r], c2, nm));
+          psum += p[r];
+        }
+        l_part += psum;
+        LDS_AS char* pb = p_buf(i, par, d);
+        if constexpr (NG == 1) {
+          // P' = f16(p * key scale) in the A-operand order of the PV MFMA
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            f16x8 pa;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pa[e] = (_Float16)(p[8 * hh + e] * sv16[8 * hh + e]);
+            *(LDS_AS f16x8*)(pb + 1024 * hh + 16 * lane) = pa;
+          }
+        } else {
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            *(LDS_AS f32x4*)(pb + 1024 * qq + 16 * lane) = f32x4{p[4 * qq], p[4 * qq + 1], p[4 * qq + 2], p[4 * qq + 3]};
+        }
+      }
+      __syncthreads();          // end of step
     }
     const float l_row = halves_sum(l_part);
     if (g == 0) {
+      LDS_AS float* st = stats(d);
       st[par * kRows + n] = m_run;
       st[(2 + par) * kRows + n] = l_row;
     }
@@ -488,110 +528,143 @@ mla_decode_kernel(DecodeArgs a) {
   }
 
   // ================================================================ value waves
-  const int vc = sub & 1;             // value wave owns columns [256 vc, 256 vc + 256) of group rgl
+  const int vq4 = sub;                // value wave owns columns [128 vq4, 128 vq4 + 128) of both groups
   // O holds sum_j 2^(c2 (x_j - mO)) s_j v_j for the row's reference max mO,
   // kept per row in LDS (C-layout rows 8(r/4) + 4g + r%4) and in a register
   // for the lane's A-layout row n.
-  LDS_AS float* const mo_lds = (LDS_AS float*)(L0 + LY::kMO) + kRows * sub;
-  float mo_a = kNegInf;
-  if (g == 0) mo_lds[n] = kNegInf;
+  LDS_AS float* const mo_lds = (LDS_AS float*)(L0 + LY::kMO) + 2 * kRows * sub;   // [row group][32]
+  float mo_a[2] = {kNegInf, kNegInf};
+  if (g == 0) { mo_lds[n] = kNegInf; mo_lds[kRows + n] = kNegInf; }
   // V read (B operand via transpose read): provider lane p = 2k + h of each 16-lane
   // group addresses key tau(g,k) = 4g + (k&3) + 8(k>>2) at column 32nb + 16q + 8h.
   const int vq = (lane >> 4) & 1, vk = (lane & 15) >> 1, vh = lane & 1;
   const int vtau = 4 * g + (vk & 3) + 8 * (vk >> 2);
   const uint32_t vread0 = (uint32_t)(16 * (4 * vtau + ((0 + vq) ^ ((vtau >> 2) & 3))) + 8 * vh);
   const uint32_t vread1 = (uint32_t)(16 * (4 * vtau + ((2 + vq) ^ ((vtau >> 2) & 3))) + 8 * vh);
-  f32x16 o[8];
+  f32x16 o[2][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = f32x16{};
-  copy_pages();
-  __syncthreads();              // the page copy is visible
-  if (nsteps > 0) issue_step(0);
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[r][i] = f32x16{};
+  if (nsteps > 0) {
+    fetch_window(0);
+    issue_step(0);
+  }
   wait_vmcnt<0>();              // this wave's share of step 0 has landed
   __syncthreads();
 
-  // P' (f16, NG == 1) or p (fp32, NG == 9) of one tile in this lane's A-operand
-  // order, as raw dwords read from LDS at the top of a step.
+  // P' (f16, NG == 1) or p (fp32, NG == 9) of one tile and row group in this
+  // lane's A-operand order, as raw dwords.
   typedef u32x4 PRaw[NG == 1 ? 2 : 4];
   auto load_p = [&](LDS_AS const char* pb, PRaw& pr) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < (NG == 1 ? 2 : 4); ++k) pr[k] = *(LDS_AS const u32x4*)(pb + 1024 * k + 16 * lane);
   };
-  // One score wave's tile: bring O and the tile's P' to a common reference
-  // (rare: only when a reference moved), then O += P' V.
-  auto value_tile = [&](LDS_AS const char* tb, LDS_AS const char* sb, LDS_AS const float* ab, float mt,
-                        const PRaw& pr) __attribute__((always_inline)) {
+  // Bring O of row group r and the tile's P' to a common reference (rare: only
+  // when a reference moved); returns the factor for the tile's P' (1 if none).
+  auto align_ref = [&](int r, LDS_AS const float* ab, float mt, bool& scale_p) __attribute__((always_inline)) -> float {
     float pf = 1.0f;
-    bool scale_p = false;
-    if (wave_any(mt != mo_a)) {
-      const float m_new = fmaxf(mo_a, mt);
-      if (wave_any(m_new != mo_a)) {
+    scale_p = false;
+    if (wave_any(mt != mo_a[r])) {
+      const float m_new = fmaxf(mo_a[r], mt);
+      if (wave_any(m_new != mo_a[r])) {
+        LDS_AS float* mol = mo_lds + r * kRows;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-          const f32x4 old = *(LDS_AS const f32x4*)(mo_lds + 8 * qq + 4 * g);
+          const f32x4 old = *(LDS_AS const f32x4*)(mol + 8 * qq + 4 * g);
           const f32x4 tm = *(LDS_AS const f32x4*)(ab + 8 * qq + 4 * g);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float al = old[e] == kNegInf ? 0.0f : exp2_fast((old[e] - fmaxf(old[e], tm[e])) * c2);
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) o[nb][4 * qq + e] *= al;
+            for (int nl = 0; nl < 4; ++nl) o[r][nl][4 * qq + e] *= al;
           }
         }
-        if (g == 0) mo_lds[n] = m_new;
+        if (g == 0) mol[n] = m_new;
       }
       pf = mt == kNegInf ? 0.0f : exp2_fast((mt - m_new) * c2);
       scale_p = wave_any(pf != 1.0f);
-      mo_a = m_new;
+      mo_a[r] = m_new;
     }
+    return pf;
+  };
+  // Everything one tile's PV step reads from LDS -- the V fragments (ds_read_b64_tr_b8),
+  // P' of both row groups and their reference maxima -- is fetched up front, so
+  // that the LDS latency is paid once per tile rather than per MFMA.
+  typedef i32x2 VFrag[2][4];
+  auto value_fetch = [&](int step, int tt, VFrag& vr, PRaw (&pr)[2], float (&mt)[2]) __attribute__((always_inline)) {
+    LDS_AS const char* tb = tile_buf(step, tt);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      load_p(p_buf(step, tt, r), pr[r]);
+      mt[r] = alpha_buf(step, tt, r)[n];
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int nl = 0; nl < 4; ++nl) {
+        const int nb = 4 * vq4 + nl;
+        vr[hh][nl] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (LDS_AS i32x2*)(tb + ((nb & 1) ? vread1 : vread0) + 1024 * (9 * hh + (nb >> 1))));
+      }
+  };
+  // O += P' V for one tile (both row groups), V widened once per fragment.
+  auto value_compute = [&](int step, int tt, const VFrag& vr, const PRaw (&pr)[2], const float (&mt)[2])
+      __attribute__((always_inline)) {
+    float pf[2];
+    bool sp[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) pf[r] = align_ref(r, alpha_buf(step, tt, r), mt[r], sp[r]);
     if constexpr (NG == 1) {
-      f16x8 pa[2];
+      f16x8 pa[2][2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) pa[hh] = __builtin_bit_cast(f16x8, pr[hh]);
-      if (scale_p) {
+      for (int r = 0; r < 2; ++r) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh) pa[r][hh] = __builtin_bit_cast(f16x8, pr[r][hh]);
+        if (sp[r]) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pa[hh][e] = (_Float16)((float)pa[hh][e] * pf);
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pa[r][hh][e] = (_Float16)((float)pa[r][hh][e] * pf[r]);
+        }
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-        for (int nl = 0; nl < 8; ++nl) {
-          const int nb = 8 * vc + nl;
-          const i32x2 vr = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (LDS_AS i32x2*)(tb + ((nb & 1) ? vread1 : vread0) + 1024 * (9 * hh + (nb >> 1))));
-          o[nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              pa[hh], fp8x8_to_f16((uint32_t)vr[0], (uint32_t)vr[1]), o[nl], 0, 0, 0);
+        for (int nl = 0; nl < 4; ++nl) {
+          const f16x8 vb = fp8x8_to_f16((uint32_t)vr[hh][nl][0], (uint32_t)vr[hh][nl][1]);
+          o[0][nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[0][hh], vb, o[0][nl], 0, 0, 0);
+          o[1][nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[1][hh], vb, o[1][nl], 0, 0, 0);
         }
       }
     } else {
-      float p[16];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const f32x4 pv = __builtin_bit_cast(f32x4, pr[qq]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[4 * qq + e] = pv[e] * pf;
-      }
+      LDS_AS const char* sb = scale_buf(step, tt);
       // value group gv = columns [64gv, 64gv + 64) = blocks nb = 2gv, 2gv + 1
 #pragma unroll
-      for (int gl = 0; gl < 4; ++gl) {
-        const int gv = 4 * vc + gl;
+      for (int gl = 0; gl < 2; ++gl) {
+        const int gv = 2 * vq4 + gl;
         float sv16[16];
         lane_scales(sb, gv, sv16);
-        f16x8 pa[2];
+        f16x8 pa[2][2];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int r = 0; r < 2; ++r) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pa[hh][e] = (_Float16)(p[8 * hh + e] * sv16[8 * hh + e]);
+          for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float pv = __builtin_bit_cast(f32x4, pr[r][2 * hh + (e >> 2)])[e & 3];
+              pa[r][hh][e] = (_Float16)(pv * pf[r] * sv16[8 * hh + e]);
+            }
+          }
+        }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn) {
-            const int nb = 2 * gv + nn;
-            const i32x2 vr = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (LDS_AS i32x2*)(tb + ((nb & 1) ? vread1 : vread0) + 1024 * (9 * hh + (nb >> 1))));
-            o[2 * gl + nn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                pa[hh], fp8x8_to_f16((uint32_t)vr[0], (uint32_t)vr[1]), o[2 * gl + nn], 0, 0, 0);
+            const int nl = 2 * gl + nn;
+            const f16x8 vb = fp8x8_to_f16((uint32_t)vr[hh][nl][0], (uint32_t)vr[hh][nl][1]);
+            o[0][nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[0][hh], vb, o[0][nl], 0, 0, 0);
+            o[1][nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[1][hh], vb, o[1][nl], 0, 0, 0);
           }
         }
       }
@@ -600,69 +673,82 @@ mla_decode_kernel(DecodeArgs a) {
 
   for (int i = 0; i <= nsteps; ++i) {
     if (i + 1 < nsteps) issue_step(i + 1);
-    if (i >= 1) {
-      // both tiles' hand-offs are read up front, so their LDS latency is paid once
-      // (the second tile's buffers hold stale data when it does not exist)
-      PRaw p0, p1;
-      const float mt0 = alpha_buf(i - 1, 0, rgl)[n], mt1 = alpha_buf(i - 1, 1, rgl)[n];
-      load_p(p_buf(i - 1, 0, rgl), p0);
-      load_p(p_buf(i - 1, 1, rgl), p1);
-      value_tile(tile_buf(i - 1, 0), scale_buf(i - 1, 0), alpha_buf(i - 1, 0, rgl), mt0, p0);
-      if (2 * (i - 1) + 1 < ntiles)
-        value_tile(tile_buf(i - 1, 1), scale_buf(i - 1, 1), alpha_buf(i - 1, 1, rgl), mt1, p1);
+    const bool have0 = i >= 1, have1 = i >= 1 && 2 * (i - 1) + 1 < ntiles;
+    VFrag vr0, vr1;
+    PRaw pr0[2], pr1[2];
+    float mt0[2], mt1[2];
+    if (have0) {
+      value_fetch(i - 1, 0, vr0, pr0, mt0);
+      sched_fence();
+      value_compute(i - 1, 0, vr0, pr0, mt0);
+    }
+    // the second tile's fragments are in flight across the mid-step barrier
+    // (the group-scale variant has no registers to spare for that)
+    if (NG == 1 && have1) value_fetch(i - 1, 1, vr1, pr1, mt1);
+    __syncthreads();          // mid-step
+    if (have1) {
+      if (NG != 1) {
+        value_fetch(i - 1, 1, vr1, pr1, mt1);
+        sched_fence();
+      }
+      value_compute(i - 1, 1, vr1, pr1, mt1);
     }
     wait_vmcnt<0>();          // this wave's loads of step i + 1 have landed
-    __syncthreads();
+    __syncthreads();          // end of step
   }
-  __syncthreads();             // the score waves' (m, l) are in st
+  __syncthreads();             // the score waves' (m, l) are in the stats
 
   // O / (2^(c2 (m0 - mO)) l0 + 2^(c2 (m1 - mO)) l1) per row, mO >= m0, m1
-  float lse_n = kNegInf;       // log2-sum-exp of row n (lanes g == 0)
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    const f32x4 m0 = *(LDS_AS const f32x4*)(st + 0 * kRows + 8 * qq + 4 * g);
-    const f32x4 m1 = *(LDS_AS const f32x4*)(st + 1 * kRows + 8 * qq + 4 * g);
-    const f32x4 l0 = *(LDS_AS const f32x4*)(st + 2 * kRows + 8 * qq + 4 * g);
-    const f32x4 l1 = *(LDS_AS const f32x4*)(st + 3 * kRows + 8 * qq + 4 * g);
-    const f32x4 mo = *(LDS_AS const f32x4*)(mo_lds + 8 * qq + 4 * g);
+  for (int r = 0; r < 2; ++r) {
+    const int rg = 2 * rgp + r;
+    if (rg >= a.row_groups) break;      // the pair's second group does not exist
+    LDS_AS const float* st = stats(r);
+    LDS_AS const float* mol = mo_lds + r * kRows;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float Lt = (m0[e] == kNegInf ? 0.0f : exp2_fast((m0[e] - mo[e]) * c2) * l0[e]) +
-                       (m1[e] == kNegInf ? 0.0f : exp2_fast((m1[e] - mo[e]) * c2) * l1[e]);
-      const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+    for (int qq = 0; qq < 4; ++qq) {
+      const f32x4 m0 = *(LDS_AS const f32x4*)(st + 0 * kRows + 8 * qq + 4 * g);
+      const f32x4 m1 = *(LDS_AS const f32x4*)(st + 1 * kRows + 8 * qq + 4 * g);
+      const f32x4 l0 = *(LDS_AS const f32x4*)(st + 2 * kRows + 8 * qq + 4 * g);
+      const f32x4 l1 = *(LDS_AS const f32x4*)(st + 3 * kRows + 8 * qq + 4 * g);
+      const f32x4 mo = *(LDS_AS const f32x4*)(mol + 8 * qq + 4 * g);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) o[nb][4 * qq + e] *= inv;
-    }
-  }
-  if (g == 0) {
-    const float m0 = st[n], m1 = st[kRows + n], mo = mo_lds[n];
-    const float Lt = (m0 == kNegInf ? 0.0f : exp2_fast((m0 - mo) * c2) * st[2 * kRows + n]) +
-                     (m1 == kNegInf ? 0.0f : exp2_fast((m1 - mo) * c2) * st[3 * kRows + n]);
-    lse_n = Lt > 0.0f ? mo * c2 + __log2f(Lt) : kNegInf;
-  }
-
-  if (rg >= a.row_groups) return;    // the pair's second group does not exist
-  if (nsplit_eff == 1) {
-    // final rows: out[b, i, h, 256 vc + 32 nb + n]
+      for (int e = 0; e < 4; ++e) {
+        const float Lt = (m0[e] == kNegInf ? 0.0f : exp2_fast((m0[e] - mo[e]) * c2) * l0[e]) +
+                         (m1[e] == kNegInf ? 0.0f : exp2_fast((m1[e] - mo[e]) * c2) * l1[e]);
+        const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = rg * kRows + tile_key(r, g);
-      if (row < rows_total) {
-        uint16_t* orow = a.out + ((size_t)b * rows_total + row) * kVDim + 256 * vc;
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) orow[32 * nb + n] = f32_to_bf16_bits(o[nb][r]);
+        for (int nl = 0; nl < 4; ++nl) o[r][nl][4 * qq + e] *= inv;
       }
     }
-  } else {
-    const size_t pidx = ((size_t)b * a.row_groups + rg) * a.num_splits + split;
-    float* po = a.ws_o + pidx * kRows * kVDim + 256 * vc;
+    if (nsplit_eff == 1) {
+      // final rows: out[b, i, h, 128 vq4 + 32 nl + n]
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float* prow = po + tile_key(r, g) * kVDim;
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = rg * kRows + tile_key(rr, g);
+        if (row < rows_total) {
+          uint16_t* orow = a.out + ((size_t)b * rows_total + row) * kVDim + 128 * vq4;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) prow[32 * nb + n] = o[nb][r];
+          for (int nl = 0; nl < 4; ++nl) orow[32 * nl + n] = f32_to_bf16_bits(o[r][nl][rr]);
+        }
+      }
+    } else {
+      const size_t pidx = ((size_t)b * a.row_groups + rg) * a.num_splits + split;
+      float* po = a.ws_o + pidx * kRows * kVDim + 128 * vq4;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        float* prow = po + tile_key(rr, g) * kVDim;
+#pragma unroll
+        for (int nl = 0; nl < 4; ++nl) prow[32 * nl + n] = o[r][nl][rr];
+      }
+      if (vq4 == 0 && g == 0) {
+        // the row's log2-sum-exp: c2 mO + log2(L)
+        const float m0 = st[n], m1 = st[kRows + n], mo = mol[n];
+        const float Lt = (m0 == kNegInf ? 0.0f : exp2_fast((m0 - mo) * c2) * st[2 * kRows + n]) +
+                         (m1 == kNegInf ? 0.0f : exp2_fast((m1 - mo) * c2) * st[3 * kRows + n]);
+        a.ws_lse[pidx * kRows + n] = Lt > 0.0f ? mo * c2 + __log2f(Lt) : kNegInf;
+      }
     }
-    if (vc == 0 && g == 0) a.ws_lse[pidx * kRows + n] = lse_n;
   }
 }
 

@@ -14,12 +14,10 @@ constexpr int kTile = 32;                // keys per MFMA tile
 constexpr int kRows = 32;                // query rows (q position, head) per row group
 constexpr int kWaves = 4;                // waves per workgroup, each streaming its own tiles
 constexpr int kSplitQuantum = kTile * kWaves;   // split lengths are multiples of this
-// The decode kernel keeps the page ids of up to this many keys of its split in
-// LDS; the plan keeps splits at most this long whenever the workspace allows
-// (longer ones still decode correctly, reading the rest of the page ids from
-// the tables directly).
+// The plan keeps splits at most this long whenever the workspace allows, so
+// that long requests spread over many workgroups (any split length decodes
+// correctly).
 constexpr int kMaxSplitKeys = 8192;
-constexpr int kMaxBlocks16 = kMaxSplitKeys / 16;
 
 // Everything the main kernel needs, by value.  Offsets are precomputed on the
 // host from the contiguous row-major shapes of the blocks / scales tensors.

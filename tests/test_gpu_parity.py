@@ -109,11 +109,11 @@ def test_forced_splits(gpu_device, splits):
     check_gate(base, ref, "splits 1")
 
 
-def test_split_longer_than_the_page_copy(gpu_device):
-    """One split per request over up to 20000 keys with 16-key pages: the first
-    8192 keys' page ids come from the workgroup's LDS copy, the rest straight
-    from the tables."""
-    say("split longer than the LDS page copy")
+def test_long_split_many_page_windows(gpu_device):
+    """One split per request over up to 20000 keys with 16-key pages: the
+    workgroup walks 20 windows of 64 page-table entries, each prefetched while
+    the previous one is in use."""
+    say("long split over many page windows")
     w = _w(gpu_device, 2, 128, [9000, 20000], 16, 64, independent_scales=True, spare_blocks=3,
            spare_scale_blocks=3, seed=77, poison=True, unused_table_id=0xFFFFFFFF)
     ref = oracle_decode(w)
