@@ -172,6 +172,8 @@ __device__ __forceinline__ constexpr int tile_key(int r, int g) { return 8 * (r 
 // hand-offs.
 constexpr int kWaveCount = 8;
 constexpr int kThreads = 64 * kWaveCount;
+constexpr int kEpStride = 128 + 4;            // floats per row of a value wave's epilogue transpose
+constexpr int kEpSlice = kRows * kEpStride;   // floats of one value wave's epilogue slice
 
 template <int NG>
 struct Layout {
@@ -194,6 +196,8 @@ struct Layout {
   static constexpr int kTotal = kX + (kXOwn ? 4 * kXBytes : 0);
 };
 static_assert(Layout<1>::kTotal <= 160 * 1024 && Layout<9>::kTotal <= 160 * 1024, "LDS budget");
+static_assert(4 * kEpSlice * 4 <= 6 * kTileBytes, "epilogue transposes fit in the tile buffers");
+static_assert(2 * 2 * 18 * 64 * 16 <= 4 * kTileBytes, "q staging fits in the tile buffers of steps 1 and 2");
 
 template <int NG>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
@@ -381,24 +385,34 @@ mla_decode_kernel(DecodeArgs a) {
     // q of both row groups in the B-operand order of the 32x32x16 MFMAs: for
     // block s the two MFMAs take depths 64s + 32d + 16g + [0,8) and + [8,16) --
     // the same depths as the key bytes each lane reads.
-    bf16x8 qv[2][18];
+    // The two tile-parity waves of a depth half need the same q: each loads its
+    // own row group's share from HBM and passes it to the other through LDS
+    // (staged in the tile buffers of steps 1 and 2, which are not loaded yet).
+    bf16x8 qv[2][18], qown[18];
     {
+      const int row = (2 * rgp + par) * kRows + n;
+      const bool ok = row < rows_total;
+      const uint16_t* qrow = a.q + ((size_t)b * rows_total + (ok ? row : 0)) * kHeadDim + 32 * d + 16 * g;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int row = (2 * rgp + r) * kRows + n;
-        const bool ok = row < rows_total;
-        const uint16_t* qrow = a.q + ((size_t)b * rows_total + (ok ? row : 0)) * kHeadDim + 32 * d + 16 * g;
-#pragma unroll
-        for (int s = 0; s < 9; ++s) {
-          const u32x4* src = (const u32x4*)(qrow + 64 * s);
-          u32x4 w0 = src[0], w1 = src[1];
-          if (!ok) { w0 = u32x4{0, 0, 0, 0}; w1 = u32x4{0, 0, 0, 0}; }
-          qv[r][2 * s] = __builtin_bit_cast(bf16x8, w0);
-          qv[r][2 * s + 1] = __builtin_bit_cast(bf16x8, w1);
-        }
+      for (int s = 0; s < 9; ++s) {
+        const u32x4* src = (const u32x4*)(qrow + 64 * s);
+        u32x4 w0 = src[0], w1 = src[1];
+        if (!ok) { w0 = u32x4{0, 0, 0, 0}; w1 = u32x4{0, 0, 0, 0}; }
+        qown[2 * s] = __builtin_bit_cast(bf16x8, w0);
+        qown[2 * s + 1] = __builtin_bit_cast(bf16x8, w1);
       }
     }
-    wait_vmcnt<0>();            // q has landed
+    LDS_AS char* const qstage = L0 + LY::kTiles + 2 * kTileBytes;   // [depth half][row group][18][64 lanes][16 B]
+#pragma unroll
+    for (int j = 0; j < 18; ++j)
+      *(LDS_AS bf16x8*)(qstage + (((d * 2 + par) * 18 + j) * 64 + lane) * 16) = qown[j];
+    __syncthreads();            // q shares staged
+#pragma unroll
+    for (int j = 0; j < 18; ++j) {
+      const bf16x8 other = *(LDS_AS const bf16x8*)(qstage + (((d * 2 + (par ^ 1)) * 18 + j) * 64 + lane) * 16);
+      qv[0][j] = par ? other : qown[j];
+      qv[1][j] = par ? qown[j] : other;
+    }
     __syncthreads();            // step 0 has landed (the value waves waited for their loads)
 
     for (int i = 0; i <= nsteps; ++i) {
@@ -550,6 +564,7 @@ mla_decode_kernel(DecodeArgs a) {
     fetch_window(0);
     issue_step(0);
   }
+  __syncthreads();              // (the score waves stage q)
   wait_vmcnt<0>();              // this wave's share of step 0 has landed
   __syncthreads();
 
@@ -560,45 +575,53 @@ mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < (NG == 1 ? 2 : 4); ++k) pr[k] = *(LDS_AS const u32x4*)(pb + 1024 * k + 16 * lane);
   };
-  // Bring O of row group r and the tile's P' to a common reference (rare: only
-  // when a reference moved); returns the factor for the tile's P' (1 if none).
-  auto align_ref = [&](int r, LDS_AS const float* ab, float mt, bool& scale_p) __attribute__((always_inline)) -> float {
-    float pf = 1.0f;
-    scale_p = false;
-    if (wave_any(mt != mo_a[r])) {
-      const float m_new = fmaxf(mo_a[r], mt);
+  // Bring O of row group r and both tiles of a step to one reference per row,
+  // max(O's, tile 0's, tile 1's): O is rescaled at most once per step, and
+  // only when a reference moved (rare: references move lazily); the factors
+  // for the tiles' P' come back in pf (1 when nothing changes).
+  auto align_step = [&](int r, int step, bool two, const float (&mt)[2], float (&pf)[2], bool (&sp)[2])
+      __attribute__((always_inline)) {
+    pf[0] = pf[1] = 1.0f;
+    sp[0] = sp[1] = false;
+    const float mt1 = two ? mt[1] : kNegInf;
+    const float m_new = fmaxf(mo_a[r], fmaxf(mt[0], mt1));
+    if (wave_any(mt[0] != mo_a[r] || (two && mt1 != mo_a[r]))) {
       if (wave_any(m_new != mo_a[r])) {
         LDS_AS float* mol = mo_lds + r * kRows;
+        LDS_AS const float* a0 = alpha_buf(step, 0, r);
+        LDS_AS const float* a1 = alpha_buf(step, 1, r);
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const f32x4 old = *(LDS_AS const f32x4*)(mol + 8 * qq + 4 * g);
-          const f32x4 tm = *(LDS_AS const f32x4*)(ab + 8 * qq + 4 * g);
+          const f32x4 t0 = *(LDS_AS const f32x4*)(a0 + 8 * qq + 4 * g);
+          const f32x4 t1 = two ? *(LDS_AS const f32x4*)(a1 + 8 * qq + 4 * g) : f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float al = old[e] == kNegInf ? 0.0f : exp2_fast((old[e] - fmaxf(old[e], tm[e])) * c2);
+            const float nw = fmaxf(old[e], fmaxf(t0[e], t1[e]));
+            const float al = old[e] == kNegInf ? 0.0f : exp2_fast((old[e] - nw) * c2);
 #pragma unroll
             for (int nl = 0; nl < 4; ++nl) o[r][nl][4 * qq + e] *= al;
           }
         }
         if (g == 0) mol[n] = m_new;
       }
-      pf = mt == kNegInf ? 0.0f : exp2_fast((mt - m_new) * c2);
-      scale_p = wave_any(pf != 1.0f);
+      pf[0] = mt[0] == kNegInf ? 0.0f : exp2_fast((mt[0] - m_new) * c2);
+      pf[1] = mt1 == kNegInf ? 0.0f : exp2_fast((mt1 - m_new) * c2);
+      sp[0] = wave_any(pf[0] != 1.0f);
+      sp[1] = two && wave_any(pf[1] != 1.0f);
       mo_a[r] = m_new;
     }
-    return pf;
   };
-  // Everything one tile's PV step reads from LDS -- the V fragments (ds_read_b64_tr_b8),
-  // P' of both row groups and their reference maxima -- is fetched up front, so
-  // that the LDS latency is paid once per tile rather than per MFMA.
+  // Everything a tile's PV step reads from LDS -- the V fragments (ds_read_b64_tr_b8),
+  // P' of both row groups and their reference maxima -- is fetched ahead of the
+  // MFMAs, so that the LDS latency is not paid per MFMA.
   typedef i32x2 VFrag[2][4];
-  auto value_fetch = [&](int step, int tt, VFrag& vr, PRaw (&pr)[2], float (&mt)[2]) __attribute__((always_inline)) {
-    LDS_AS const char* tb = tile_buf(step, tt);
+  auto fetch_p = [&](int step, int tt, PRaw (&pr)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      load_p(p_buf(step, tt, r), pr[r]);
-      mt[r] = alpha_buf(step, tt, r)[n];
-    }
+    for (int r = 0; r < 2; ++r) load_p(p_buf(step, tt, r), pr[r]);
+  };
+  auto fetch_v = [&](int step, int tt, VFrag& vr) __attribute__((always_inline)) {
+    LDS_AS const char* tb = tile_buf(step, tt);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -608,90 +631,133 @@ mla_decode_kernel(DecodeArgs a) {
             (LDS_AS i32x2*)(tb + ((nb & 1) ? vread1 : vread0) + 1024 * (9 * hh + (nb >> 1))));
       }
   };
-  // O += P' V for one tile (both row groups), V widened once per fragment.
-  auto value_compute = [&](int step, int tt, const VFrag& vr, const PRaw (&pr)[2], const float (&mt)[2])
+  // Per-token scales: the VALU part of a tile (P' brought to the step's
+  // reference, V widened to f16) ...
+  auto prep_p = [&](const PRaw (&pr)[2], const float (&pf)[2], const bool (&sp)[2], f16x8 (&pa)[2][2])
       __attribute__((always_inline)) {
-    float pf[2];
-    bool sp[2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) pf[r] = align_ref(r, alpha_buf(step, tt, r), mt[r], sp[r]);
-    if constexpr (NG == 1) {
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) pa[r][hh] = __builtin_bit_cast(f16x8, pr[r][hh]);
+      if (sp[r]) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pa[r][hh][e] = (_Float16)((float)pa[r][hh][e] * pf[r]);
+      }
+    }
+  };
+  auto widen_v = [&](const VFrag& vr, f16x8 (&vb)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int nl = 0; nl < 4; ++nl) vb[hh][nl] = fp8x8_to_f16((uint32_t)vr[hh][nl][0], (uint32_t)vr[hh][nl][1]);
+  };
+  // ... and its MFMA part, O += P' V for both row groups.
+  auto mma_tile = [&](const f16x8 (&pa)[2][2], const f16x8 (&vb)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int nl = 0; nl < 4; ++nl) {
+        o[0][nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[0][hh], vb[hh][nl], o[0][nl], 0, 0, 0);
+        o[1][nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[1][hh], vb[hh][nl], o[1][nl], 0, 0, 0);
+      }
+  };
+  // Group scales: one tile, P'_g = f16(p * s_g) per value group, then O += P'_g V.
+  auto compute_tile_g = [&](int step, int tt, const VFrag& vr, const PRaw (&pr)[2], const float (&pf)[2])
+      __attribute__((always_inline)) {
+    LDS_AS const char* sb = scale_buf(step, tt);
+    // value group gv = columns [64gv, 64gv + 64) = blocks nb = 2gv, 2gv + 1
+#pragma unroll
+    for (int gl = 0; gl < 2; ++gl) {
+      const int gv = 2 * vq4 + gl;
+      float sv16[16];
+      lane_scales(sb, gv, sv16);
       f16x8 pa[2][2];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) pa[r][hh] = __builtin_bit_cast(f16x8, pr[r][hh]);
-        if (sp[r]) {
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pa[r][hh][e] = (_Float16)((float)pa[r][hh][e] * pf[r]);
+          for (int e = 0; e < 8; ++e) {
+            const float pv = __builtin_bit_cast(f32x4, pr[r][2 * hh + (e >> 2)])[e & 3];
+            pa[r][hh][e] = (_Float16)(pv * pf[r] * sv16[8 * hh + e]);
+          }
         }
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-        for (int nl = 0; nl < 4; ++nl) {
+        for (int nn = 0; nn < 2; ++nn) {
+          const int nl = 2 * gl + nn;
           const f16x8 vb = fp8x8_to_f16((uint32_t)vr[hh][nl][0], (uint32_t)vr[hh][nl][1]);
           o[0][nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[0][hh], vb, o[0][nl], 0, 0, 0);
           o[1][nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[1][hh], vb, o[1][nl], 0, 0, 0);
         }
       }
-    } else {
-      LDS_AS const char* sb = scale_buf(step, tt);
-      // value group gv = columns [64gv, 64gv + 64) = blocks nb = 2gv, 2gv + 1
-#pragma unroll
-      for (int gl = 0; gl < 2; ++gl) {
-        const int gv = 2 * vq4 + gl;
-        float sv16[16];
-        lane_scales(sb, gv, sv16);
-        f16x8 pa[2][2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float pv = __builtin_bit_cast(f32x4, pr[r][2 * hh + (e >> 2)])[e & 3];
-              pa[r][hh][e] = (_Float16)(pv * pf[r] * sv16[8 * hh + e]);
-            }
-          }
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int nn = 0; nn < 2; ++nn) {
-            const int nl = 2 * gl + nn;
-            const f16x8 vb = fp8x8_to_f16((uint32_t)vr[hh][nl][0], (uint32_t)vr[hh][nl][1]);
-            o[0][nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[0][hh], vb, o[0][nl], 0, 0, 0);
-            o[1][nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[1][hh], vb, o[1][nl], 0, 0, 0);
-          }
-        }
-      }
     }
   };
 
+  // Phase 1 of a step (the score waves run their QK MFMAs): issue the next
+  // step's loads, fetch the previous step's tiles from LDS and do their VALU
+  // work.  Phase 2 (the score waves run the softmax): the PV MFMAs.
   for (int i = 0; i <= nsteps; ++i) {
     if (i + 1 < nsteps) issue_step(i + 1);
     const bool have0 = i >= 1, have1 = i >= 1 && 2 * (i - 1) + 1 < ntiles;
-    VFrag vr0, vr1;
-    PRaw pr0[2], pr1[2];
-    float mt0[2], mt1[2];
+    float pf[2][2];           // [row group][tile]
+    bool sp[2][2];
     if (have0) {
-      value_fetch(i - 1, 0, vr0, pr0, mt0);
-      sched_fence();
-      value_compute(i - 1, 0, vr0, pr0, mt0);
-    }
-    // the second tile's fragments are in flight across the mid-step barrier
-    // (the group-scale variant has no registers to spare for that)
-    if (NG == 1 && have1) value_fetch(i - 1, 1, vr1, pr1, mt1);
-    __syncthreads();          // mid-step
-    if (have1) {
-      if (NG != 1) {
-        value_fetch(i - 1, 1, vr1, pr1, mt1);
-        sched_fence();
+      float mt[2][2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        mt[r][0] = alpha_buf(i - 1, 0, r)[n];
+        mt[r][1] = alpha_buf(i - 1, 1, r)[n];
       }
-      value_compute(i - 1, 1, vr1, pr1, mt1);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) align_step(r, i - 1, have1, mt[r], pf[r], sp[r]);
+    }
+    if constexpr (NG == 1) {
+      VFrag vr0, vr1;
+      PRaw pr0[2], pr1[2];
+      f16x8 pa0[2][2], pa1[2][2], vb[2][4];
+      if (have0) {
+        fetch_v(i - 1, 0, vr0);
+        fetch_p(i - 1, 0, pr0);
+      }
+      if (have1) {
+        fetch_v(i - 1, 1, vr1);
+        fetch_p(i - 1, 1, pr1);
+      }
+      // (the second tile's V is widened in phase 2: registers)
+      if (have0) {
+        prep_p(pr0, {pf[0][0], pf[1][0]}, {sp[0][0], sp[1][0]}, pa0);
+        widen_v(vr0, vb);
+      }
+      if (have1) prep_p(pr1, {pf[0][1], pf[1][1]}, {sp[0][1], sp[1][1]}, pa1);
+      __syncthreads();          // mid-step
+      if (have0) mma_tile(pa0, vb);
+      if (have1) {
+        widen_v(vr1, vb);
+        mma_tile(pa1, vb);
+      }
+    } else {
+      // the group-scale variant has no registers to hold both tiles: one tile
+      // per phase
+      VFrag vr;
+      PRaw pr[2];
+      if (have0) {
+        fetch_v(i - 1, 0, vr);
+        fetch_p(i - 1, 0, pr);
+        sched_fence();
+        compute_tile_g(i - 1, 0, vr, pr, {pf[0][0], pf[1][0]});
+      }
+      __syncthreads();          // mid-step
+      if (have1) {
+        fetch_v(i - 1, 1, vr);
+        fetch_p(i - 1, 1, pr);
+        sched_fence();
+        compute_tile_g(i - 1, 1, vr, pr, {pf[0][1], pf[1][1]});
+      }
     }
     wait_vmcnt<0>();          // this wave's loads of step i + 1 have landed
     __syncthreads();          // end of step
@@ -721,25 +787,41 @@ mla_decode_kernel(DecodeArgs a) {
         for (int nl = 0; nl < 4; ++nl) o[r][nl][4 * qq + e] *= inv;
       }
     }
+    // Rows leave through LDS: the MFMA layout gives a lane one column of 16
+    // rows; the transposed copy lets each lane store 16 contiguous bytes.  Each
+    // value wave uses its own slice of the (now idle) tile buffers.
+    LDS_AS float* const ep = (LDS_AS float*)(L0 + LY::kTiles) + sub * kEpSlice;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+      for (int nl = 0; nl < 4; ++nl) ep[tile_key(rr, g) * kEpStride + 32 * nl + n] = o[r][nl][rr];
     if (nsplit_eff == 1) {
-      // final rows: out[b, i, h, 128 vq4 + 32 nl + n]
+      // final rows: out[b, i, h, 128 vq4 + c], 8 columns (16 bytes of bf16) per lane, 4 rows per pass
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = rg * kRows + tile_key(rr, g);
+      for (int k = 0; k < 8; ++k) {
+        const int rl = 4 * k + (lane >> 4);
+        const int c8 = 8 * (lane & 15);
+        const int row = rg * kRows + rl;
+        const f32x4 v0 = *(LDS_AS const f32x4*)(ep + rl * kEpStride + c8);
+        const f32x4 v1 = *(LDS_AS const f32x4*)(ep + rl * kEpStride + c8 + 4);
         if (row < rows_total) {
-          uint16_t* orow = a.out + ((size_t)b * rows_total + row) * kVDim + 128 * vq4;
+          u32x4 packed;
 #pragma unroll
-          for (int nl = 0; nl < 4; ++nl) orow[32 * nl + n] = f32_to_bf16_bits(o[r][nl][rr]);
+          for (int j = 0; j < 2; ++j) {
+            packed[j] = (uint32_t)f32_to_bf16_bits(v0[2 * j]) | ((uint32_t)f32_to_bf16_bits(v0[2 * j + 1]) << 16);
+            packed[2 + j] = (uint32_t)f32_to_bf16_bits(v1[2 * j]) | ((uint32_t)f32_to_bf16_bits(v1[2 * j + 1]) << 16);
+          }
+          *(u32x4*)(a.out + ((size_t)b * rows_total + row) * kVDim + 128 * vq4 + c8) = packed;
         }
       }
     } else {
       const size_t pidx = ((size_t)b * a.row_groups + rg) * a.num_splits + split;
       float* po = a.ws_o + pidx * kRows * kVDim + 128 * vq4;
+      // 4 columns (16 bytes) per lane, 2 rows per pass
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        float* prow = po + tile_key(rr, g) * kVDim;
-#pragma unroll
-        for (int nl = 0; nl < 4; ++nl) prow[32 * nl + n] = o[r][nl][rr];
+      for (int k = 0; k < 16; ++k) {
+        const int rl = 2 * k + g;
+        *(f32x4*)(po + rl * kVDim + 4 * n) = *(LDS_AS const f32x4*)(ep + rl * kEpStride + 4 * n);
       }
       if (vq4 == 0 && g == 0) {
         // the row's log2-sum-exp: c2 mO + log2(L)
@@ -783,17 +865,27 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(DecodeArgs
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
   float W = 0.0f;
   if (M != kNegInf) {
-    for (int s = 0; s < nsplit_eff; ++s) {
-      const float ls = a.ws_lse[(pbase + s) * kRows + rl];
-      if (ls == kNegInf) continue;
-      const float w = exp2_fast(ls - M);
-      W += w;
-      const f32x4* src = (const f32x4*)(a.ws_o + ((pbase + s) * kRows + rl) * kVDim + col0);
-      const f32x4 v0 = src[0], v1 = src[1];
+    // eight splits per batch: their sixteen loads are all in flight together
+    for (int s0 = 0; s0 < nsplit_eff; s0 += 8) {
+      f32x4 v[8][2];
+      float w[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[j] = __builtin_fmaf(w, v0[j], acc[j]);
-        acc[4 + j] = __builtin_fmaf(w, v1[j], acc[4 + j]);
+      for (int u = 0; u < 8; ++u) {
+        const int s = min(s0 + u, nsplit_eff - 1);
+        const float ls = a.ws_lse[(pbase + s) * kRows + rl];
+        w[u] = (s0 + u < nsplit_eff && ls != kNegInf) ? exp2_fast(ls - M) : 0.0f;
+        const f32x4* src = (const f32x4*)(a.ws_o + ((pbase + s) * kRows + rl) * kVDim + col0);
+        v[u][0] = src[0];
+        v[u][1] = src[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        W += w[u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j] = __builtin_fmaf(w[u], v[u][0][j], acc[j]);
+          acc[4 + j] = __builtin_fmaf(w[u], v[u][1][j], acc[4 + j]);
+        }
       }
     }
   }
