@@ -136,6 +136,30 @@ __device__ __forceinline__ void lds_dma4(const void* gsrc, LDS_AS void* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, ldst, 4, 0, 0);
 }
 
+// The same direct global->LDS loads written out by hand for the tile stream.
+// The compiler counts its own LDS DMA as a pending LDS write and makes every
+// later LDS read (and every workgroup barrier) wait for it; a tile loaded a
+// step ahead lands in a buffer nobody reads before the end-of-step wait, so the
+// stream is kept out of the compiler's view and waited for explicitly
+// (wait_vmcnt before the end-of-step barrier).  Writing M0 right before an LDS
+// DMA needs one wait state, hence the s_nop.
+// 16 bytes per lane from base + voff + kOff into LDS ldst + kOff + 16 * lane.
+template <int kOff>
+__device__ __forceinline__ void tile_dma16(const uint8_t* base, uint32_t voff, uint32_t ldst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
+               :: "v"(voff), "s"(base), "s"(ldst), "n"(kOff) : "memory", "m0");
+}
+// 4 bytes per lane from gsrc into LDS ldst + 4 * lane.
+__device__ __forceinline__ void tile_dma4(const void* gsrc, uint32_t ldst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gsrc), "s"(ldst) : "memory", "m0");
+}
+
+// Workgroup barrier for LDS hand-offs only: this wave's LDS accesses are
+// complete, then s_barrier.  Unlike __syncthreads it does not wait for vector
+// memory, so tile loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Key position (within a 32-key tile) held by accumulator register r of an
 // S^T = K Q^T 32x32 MFMA result, for lane half g = lane / 32.
 __device__ __forceinline__ constexpr int tile_key(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
@@ -306,43 +330,51 @@ mla_decode_kernel(DecodeArgs a) {
   // blocks), and the scales of that tile when it loads half 0.  Keys at or past
   // t_hi are never read: their lanes re-load the last valid key (finite data
   // that the softmax masks out), so slots, pages and table columns past a
-  // request's length stay untouched.
-  auto issue_step = [&](int step) __attribute__((always_inline)) {
+  // request's length stay untouched.  The nine block loads go out in three
+  // parts of three, spread over the step, so that no wave stalls long on a full
+  // memory pipeline and the request stream stays even.
+  // source of the pending loads: a wave-uniform block-row base plus this lane's
+  // 32-bit offset (scalar-base addressing)
+  const uint8_t* dma_base = layer_base;
+  uint32_t dma_voff = 0;
+  auto issue_part = [&](int step, int part) __attribute__((always_inline)) {
     const int tt = sub >> 1, hb = sub & 1;
     const int j = 2 * step + tt;
     if (j >= ntiles) return;
-    const int t0 = t_lo + kTile * j;
-    const int nvalid = min(kTile, t_hi - t0);     // >= 1
-    if ((step >> 4) != cur_win) enter_window(step >> 4);
-    const int blk0 = ((t0 - t_lo) >> 4) & 63;     // lane of the tile's first block in the window
     LDS_AS char* dst = tile_buf(step, tt) + 1024 * 9 * hb;
-    const int bh = nvalid > 16 ? 1 : 0;           // block of the second half (clamped)
-    {
+    if (part == 0) {
+      const int t0 = t_lo + kTile * j;
+      const int nvalid = min(kTile, t_hi - t0);     // >= 1
+      if ((step >> 4) != cur_win) enter_window(step >> 4);
+      const int blk0 = ((t0 - t_lo) >> 4) & 63;     // lane of the tile's first block in the window
+      const int bh = nvalid > 16 ? 1 : 0;           // block of the second half (clamped)
       const int kk = min(16 * hb + ld_key, nvalid - 1);
       const int half = __builtin_amdgcn_readfirstlane(min(hb, bh));   // half holding this wave's keys
-      const uint8_t* src = layer_base + lane_u64(w_off, blk0 + half) +
-                           (size_t)(uint32_t)(kk - 16 * half) * kHeadDim + 16 * ld_col;
-      // The nine loads share one address register: column block cb sits 64 B
-      // further in HBM, given by the instruction's immediate offset.  That
-      // offset also moves the LDS address, so the LDS base steps by 1024 - 64.
-#define MLA_DMA_CB(cb) lds_dma16_off<64 * (cb)>(src, dst + (1024 - 64) * (cb))
-      MLA_DMA_CB(0); MLA_DMA_CB(1); MLA_DMA_CB(2); MLA_DMA_CB(3); MLA_DMA_CB(4);
-      MLA_DMA_CB(5); MLA_DMA_CB(6); MLA_DMA_CB(7); MLA_DMA_CB(8);
-#undef MLA_DMA_CB
-    }
-    if (hb == 0) {
-      LDS_AS char* sdst = scale_buf(step, tt);
-      const int key = min(lane & 31, nvalid - 1);
-      const uint64_t so0 = lane_u64(w_soff, blk0), so1 = lane_u64(w_soff, blk0 + bh);
-      const float* srow = slayer_base + ((key >> 4) ? so1 : so0) + (size_t)(key & 15) * NG;
-      if constexpr (NG == 1) {
-        lds_dma4(srow, sdst);
-      } else {
-        // [group][key] layout: lane covers group 2i + lane/32 for key lane%32
+      dma_base = layer_base + lane_u64(w_off, blk0 + half);
+      dma_voff = (uint32_t)(kk - 16 * half) * kHeadDim + 16 * ld_col;
+      if (hb == 0) {
+        LDS_AS char* sdst = scale_buf(step, tt);
+        const int key = min(lane & 31, nvalid - 1);
+        const uint64_t so0 = lane_u64(w_soff, blk0), so1 = lane_u64(w_soff, blk0 + bh);
+        const float* srow = slayer_base + ((key >> 4) ? so1 : so0) + (size_t)(key & 15) * NG;
+        const uint32_t sd = (uint32_t)(uintptr_t)sdst;
+        if constexpr (NG == 1) {
+          tile_dma4(srow, sd);
+        } else {
+          // [group][key] layout: lane covers group 2i + lane/32 for key lane%32
 #pragma unroll
-        for (int i = 0; i < 5; ++i) lds_dma4(srow + min(2 * i + (lane >> 5), NG - 1), sdst + 256 * i);
+          for (int i = 0; i < 5; ++i) tile_dma4(srow + min(2 * i + (lane >> 5), NG - 1), sd + 256 * i);
+        }
       }
     }
+    // The three loads of a part share one address register: column block cb
+    // sits 64 B further in HBM, given by the instruction's immediate offset.
+    // That offset also moves the LDS address, so the LDS base steps by 1024 - 64.
+#define MLA_DMA_CB(cb) tile_dma16<64 * (cb)>(dma_base, dma_voff, (uint32_t)(uintptr_t)dst + (1024 - 64) * (cb))
+    if (part == 0) { MLA_DMA_CB(0); MLA_DMA_CB(1); MLA_DMA_CB(2); }
+    if (part == 1) { MLA_DMA_CB(3); MLA_DMA_CB(4); MLA_DMA_CB(5); }
+    if (part == 2) { MLA_DMA_CB(6); MLA_DMA_CB(7); MLA_DMA_CB(8); }
+#undef MLA_DMA_CB
   };
 
   // Scales of the 16 keys a lane holds in the S^T layout: per-key (NG == 1) or
@@ -465,7 +497,7 @@ mla_decode_kernel(DecodeArgs a) {
         for (int qq = 0; qq < 4; ++qq)
           *(LDS_AS f32x4*)(xo + 1024 * qq + 16 * lane) = f32x4{give[4 * qq], give[4 * qq + 1], give[4 * qq + 2], give[4 * qq + 3]};
       }
-      __syncthreads();          // mid-step: partial scores exchanged
+      lds_barrier();            // mid-step: partial scores exchanged
       // ---- phase 2: row group d of this tile: full scores, online softmax, P'
       if (have) {
         LDS_AS const char* xi = x_buf(i, par, d);
@@ -529,7 +561,7 @@ mla_decode_kernel(DecodeArgs a) {
             *(LDS_AS f32x4*)(pb + 1024 * qq + 16 * lane) = f32x4{p[4 * qq], p[4 * qq + 1], p[4 * qq + 2], p[4 * qq + 3]};
         }
       }
-      __syncthreads();          // end of step
+      lds_barrier();            // end of step
     }
     const float l_row = halves_sum(l_part);
     if (g == 0) {
@@ -562,7 +594,9 @@ mla_decode_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) o[r][i] = f32x16{};
   if (nsteps > 0) {
     fetch_window(0);
-    issue_step(0);
+    issue_part(0, 0);
+    issue_part(0, 1);
+    issue_part(0, 2);
   }
   __syncthreads();              // (the score waves stage q)
   wait_vmcnt<0>();              // this wave's share of step 0 has landed
@@ -698,11 +732,20 @@ mla_decode_kernel(DecodeArgs a) {
     }
   };
 
-  // Phase 1 of a step (the score waves run their QK MFMAs): issue the next
-  // step's loads, fetch the previous step's tiles from LDS and do their VALU
-  // work.  Phase 2 (the score waves run the softmax): the PV MFMAs.
+  // Phase 1 of a step (the score waves run their QK MFMAs): fetch the previous
+  // step's tiles from LDS and do their VALU work.  Phase 2 (the score waves run
+  // the softmax): the PV MFMAs.  The next step's loads go out in three parts
+  // across phase 1.
   for (int i = 0; i <= nsteps; ++i) {
-    if (i + 1 < nsteps) issue_step(i + 1);
+    const bool next = i + 1 < nsteps;
+    if (next) issue_part(i + 1, 0);
+    if constexpr (NG != 1) {
+      // (the group-scale variant is short of registers to spread its loads)
+      if (next) {
+        issue_part(i + 1, 1);
+        issue_part(i + 1, 2);
+      }
+    }
     const bool have0 = i >= 1, have1 = i >= 1 && 2 * (i - 1) + 1 < ntiles;
     float pf[2][2];           // [row group][tile]
     bool sp[2][2];
@@ -728,13 +771,18 @@ mla_decode_kernel(DecodeArgs a) {
         fetch_v(i - 1, 1, vr1);
         fetch_p(i - 1, 1, pr1);
       }
+      sched_fence();
+      if (next) issue_part(i + 1, 1);
+      sched_fence();
       // (the second tile's V is widened in phase 2: registers)
       if (have0) {
         prep_p(pr0, {pf[0][0], pf[1][0]}, {sp[0][0], sp[1][0]}, pa0);
         widen_v(vr0, vb);
       }
       if (have1) prep_p(pr1, {pf[0][1], pf[1][1]}, {sp[0][1], sp[1][1]}, pa1);
-      __syncthreads();          // mid-step
+      sched_fence();
+      if (next) issue_part(i + 1, 2);
+      lds_barrier();            // mid-step
       if (have0) mma_tile(pa0, vb);
       if (have1) {
         widen_v(vr1, vb);
@@ -751,7 +799,7 @@ mla_decode_kernel(DecodeArgs a) {
         sched_fence();
         compute_tile_g(i - 1, 0, vr, pr, {pf[0][0], pf[1][0]});
       }
-      __syncthreads();          // mid-step
+      lds_barrier();            // mid-step
       if (have1) {
         fetch_v(i - 1, 1, vr);
         fetch_p(i - 1, 1, pr);
@@ -760,7 +808,7 @@ mla_decode_kernel(DecodeArgs a) {
       }
     }
     wait_vmcnt<0>();          // this wave's loads of step i + 1 have landed
-    __syncthreads();          // end of step
+    lds_barrier();            // end of step
   }
   __syncthreads();             // the score waves' (m, l) are in the stats
 
