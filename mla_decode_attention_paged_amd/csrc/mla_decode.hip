@@ -734,14 +734,14 @@ mla_decode_kernel(DecodeArgs a) {
 
   // Phase 1 of a step (the score waves run their QK MFMAs): fetch the previous
   // step's tiles from LDS and do their VALU work.  Phase 2 (the score waves run
-  // the softmax): the PV MFMAs.  The next step's loads go out in three parts
-  // across phase 1.
+  // the softmax): the PV MFMAs.  The next step's loads go out in phase 1.
   for (int i = 0; i <= nsteps; ++i) {
     const bool next = i + 1 < nsteps;
-    if (next) issue_part(i + 1, 0);
     if constexpr (NG != 1) {
-      // (the group-scale variant is short of registers to spread its loads)
+      // (the group-scale variant is short of registers to hold its tile reads
+      // across the loads: they go out first)
       if (next) {
+        issue_part(i + 1, 0);
         issue_part(i + 1, 1);
         issue_part(i + 1, 2);
       }
@@ -771,8 +771,13 @@ mla_decode_kernel(DecodeArgs a) {
         fetch_v(i - 1, 1, vr1);
         fetch_p(i - 1, 1, pr1);
       }
+      // the first two parts of the next step's loads go out while the tile
+      // reads are in flight, the third at the end of the phase
       sched_fence();
-      if (next) issue_part(i + 1, 1);
+      if (next) {
+        issue_part(i + 1, 0);
+        issue_part(i + 1, 1);
+      }
       sched_fence();
       // (the second tile's V is widened in phase 2: registers)
       if (have0) {
