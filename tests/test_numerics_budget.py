@@ -1,7 +1,7 @@
 """Rounding budget of the GPU recipe, emulated on the CPU against the oracle.
 
-The HIP kernel computes: q in f16 (exact for bf16 inputs of normal magnitude),
-E4M3FN codes widened to f16 (exact), QK^T with fp32 accumulation, the fp32
+The HIP kernel computes: QK^T with exact operands (q as given in bf16, E4M3FN
+codes widened exactly to bf16) and fp32 accumulation, the fp32
 scale applied to score columns (one scale per key) or to 64-deep group partial
 sums, an fp32 base-2 softmax, P' = f16(p * scale) against the unscaled FP8
 value codes, fp32 accumulation of P'V and of the row sums, and one final
@@ -53,24 +53,24 @@ def emulate(w, p_round="f16", k_mode="exact"):
         rows = resolve(lt[b:b + 1], None if slt is None else slt[b:b + 1], [L], P)[0]
         codes = blocks[rows[:, 0], 0, w.layer_idx, rows[:, 1], 0, :]            # [L, D]
         sc = scales[rows[:, 2], 0, w.layer_idx, rows[:, 1], 0, :].astype(np.float64)   # [L, NG]
-        Kq = E4M3FN_TABLE[codes]                                                # exact in f16
+        Kq = E4M3FN_TABLE[codes]                                                # exact in bf16
         for i in range(Q):
             n = L - Q + i + 1
             if n <= 0:
                 continue
-            q16 = _f16(q[b, i])                                                  # [H, D]
+            qx = q[b, i]                                                         # [H, D], bf16 values
             if NG == 1:
-                S = _f32(q16 @ Kq[:n].T)                                         # fp32 accumulate
+                S = _f32(qx @ Kq[:n].T)                                         # fp32 accumulate
                 x = _f32(_f32(S * sc[:n, 0][None, :]) * sm_log2)
             elif k_mode == "exact":
                 S = np.zeros((H, n))
                 for g in range(NG):
-                    T = _f32(q16[:, g * G:(g + 1) * G] @ Kq[:n, g * G:(g + 1) * G].T)
+                    T = _f32(qx[:, g * G:(g + 1) * G] @ Kq[:n, g * G:(g + 1) * G].T)
                     S = _f32(S + T * sc[:n, g][None, :])
                 x = _f32(S * sm_log2)
             else:   # K dequantised to f16 before QK (not used by the kernel)
                 K16 = _f16(Kq[:n] * _f16(np.repeat(sc[:n], G, axis=1)))
-                S = _f32(q16 @ K16.T)
+                S = _f32(qx @ K16.T)
                 x = _f32(S * sm_log2)
             m = x.max(axis=1, keepdims=True)
             p = _f32(np.exp2(x - m))
