@@ -31,13 +31,23 @@ MALL_BYTES = 256 << 20
 WORKLOADS = ("uniform", "ragged", "long1", "long4", "spec", "tiny")
 KERNEL_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "mla_decode.hip")
 
-# HBM bytes per main-kernel launch read from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE on `bench.py --steps 5 --warmup 2 --no-cpu-baseline`, each
-# divided by the factor the same counter shows for a plain copy of known size
-# (`bench.py --calibrate-copy`).  Keyed by the SHA-256 of the kernel source the
-# counters were taken on: any later edit of the kernel makes the figure stale,
-# and bench then reports traffic as null.
-MEASURED_TRAFFIC = {}
+# HBM traffic of one main-kernel launch, from two rocprofv3 --pmc runs of
+# `bench.py --steps 5 --warmup 2 --no-cpu-baseline` (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch, averaged over the dispatches), each scaled by
+# what the same counter reads for a plain 1 GiB device copy
+# (`bench.py --calibrate-copy`: FETCH_SIZE 524,302.5 KiB and WRITE_SIZE
+# 1,048,576 KiB for 1,048,576 KiB moved).  The writes are the split partials
+# (workspace), not part of the algorithmic bytes.  Keyed by the SHA-256 of the
+# device code the counters were taken on (kernel_digest): any later edit of a
+# kernel makes the figure stale and bench reports traffic as null.
+_COPY_KIB = 1048576.0
+_FETCH_PER_KIB = 524302.5 / _COPY_KIB
+_WRITE_PER_KIB = 1048576.0 / _COPY_KIB
+MEASURED_TRAFFIC = {
+    "8e7bc20e1701b4867cb667059d81c8943d7f944ddde96df6ee4a8394764ec941": {
+        "uniform_b16_l4096": {"fetch_kib": 19944.34, "write_kib": 33344.0},
+    },
+}
 
 
 def log(*a):
@@ -121,9 +131,24 @@ class HipEvents:
 
 
 def kernel_digest():
+    """SHA-256 of the device code in the kernel source (everything between the
+    first device helper and the host launchers)."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(KERNEL_SRC, "r") as f:
+        src = f.read()
+    a = src.index("// ---------------------------------------------------------------- page resolution")
+    b = src.index("// ---------------------------------------------------------------- host launchers")
+    return hashlib.sha256(src[a:b].encode()).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per main-kernel launch (read, written, total), or None."""
+    m = MEASURED_TRAFFIC.get(kernel_digest(), {}).get(workload)
+    if m is None:
+        return None
+    rd = m["fetch_kib"] * 1024 / _FETCH_PER_KIB
+    wr = m["write_kib"] * 1024 / _WRITE_PER_KIB
+    return {"read_bytes": rd, "write_bytes": wr, "total_bytes": rd + wr}
 
 
 def calibrate_copy(n_bytes=1 << 30, reps=3):
@@ -223,6 +248,7 @@ def main():
     log(f"bench: {ms_per_step * 1e3:.1f} us/step, main kernel {kern_avg_ms * 1e3:.1f} us "
         f"(min {min(kern_ms) * 1e3:.1f}), {tflops:.0f} TFLOP/s, {gbs:.0f} GB/s algorithmic")
 
+    traffic = measured_traffic(w.name)
     result = {
         "metric": "MLA decode KV tokens/s + achieved GB/s & MFMA util vs roofline, 1 MI355X",
         "value": kv_tokens / (ms_per_step * 1e-3),
@@ -234,14 +260,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3-kv/f16-mfma/fp32-acc",
+        "dtype": "fp8e4m3-kv/bf16+f16-mfma/fp32-acc",
         "data": "synthetic (seeded; N(0,1) x LogNormal(0,0.5) latent rows quantised to E4M3FN)",
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "num_heads": w.num_heads,
                    "page_size": w.page_size, "granularity": w.granularity,
                    "kv_tokens_per_step": kv_tokens, "layers_rotated": len(layers), "plan": plan},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_MFMA16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_MFMA16_TFLOPS,
-                     "traffic": MEASURED_TRAFFIC.get(kernel_digest(), {}).get(w.name),
+                     "traffic": (traffic or {}).get("total_bytes"),
+                     "traffic_detail": traffic,
                      "kernel": "mla_decode_kernel", "kernel_avg_us": kern_avg_ms * 1e3,
                      "alg_flops_per_launch": alg_flops, "alg_bytes_per_launch": alg_bytes,
                      "alg_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS},

@@ -140,10 +140,13 @@ mla_status mla_decode_paged_fp8_splits(const void* q, const void* blocks, const 
                                        size_t workspace_bytes, int32_t num_splits,
                                        hipStream_t stream);
 
-/* Same as mla_decode_paged_fp8_splits, and additionally records `main_begin`
- * and `main_end` (caller-created HIP events, either may be NULL) on `stream`
- * immediately before and after the main decode kernel, i.e. excluding the
- * split-combine kernel.  For callers that time the main kernel on its own. */
+/* Same as mla_decode_paged_fp8_splits, and additionally times the main decode
+ * kernel alone (not the split combine): when both `main_begin` and `main_end`
+ * (caller-created HIP events) are given, the kernel is launched with
+ * hipExtLaunchKernel so that the events carry its own start and end
+ * timestamps; when only one is given it is recorded on `stream` right before
+ * (begin) or after (end) the kernel.  NULL events are ignored.  For callers
+ * that time the main kernel on its own. */
 mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, const float* scales,
                                          const uint32_t* lookup_table,
                                          const uint32_t* scales_lookup_table,

@@ -24,6 +24,7 @@
 //     split across workgroups, an fp32 partial (O / l, log2-sum-exp) that
 //     mla_combine merges.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include "mla_internal.h"
 
@@ -979,7 +980,7 @@ size_t partial_bytes(int64_t batch, int64_t row_groups, int64_t num_splits) {
 }
 
 template <int NG>
-static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream, hipEvent_t begin, hipEvent_t end) {
   static bool attr_set = false;   // per process; the attribute is per function
   const int lds_bytes = Layout<NG>::kTotal;
   if (!attr_set) {
@@ -989,17 +990,25 @@ static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream) {
     attr_set = true;
   }
   const int per_xcd = (a.grid_units + 7) / 8;
-  hipLaunchKernelGGL(mla_decode_kernel<NG>, dim3(8 * per_xcd), dim3(kThreads), lds_bytes, stream, a);
+  if (begin && end) {
+    // the events take the kernel's own start / end timestamps
+    hipExtLaunchKernelGGL(mla_decode_kernel<NG>, dim3(8 * per_xcd), dim3(kThreads), lds_bytes, stream,
+                          begin, end, 0, a);
+  } else {
+    hipLaunchKernelGGL(mla_decode_kernel<NG>, dim3(8 * per_xcd), dim3(kThreads), lds_bytes, stream, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stream,
                          hipEvent_t main_begin, hipEvent_t main_end) {
   hipError_t e;
-  if (main_begin && (e = hipEventRecord(main_begin, stream)) != hipSuccess) return e;
-  e = scale_groups == 1 ? launch_main<1>(a, stream) : launch_main<9>(a, stream);
+  const bool both = main_begin && main_end;
+  if (main_begin && !both && (e = hipEventRecord(main_begin, stream)) != hipSuccess) return e;
+  e = scale_groups == 1 ? launch_main<1>(a, stream, main_begin, main_end)
+                        : launch_main<9>(a, stream, main_begin, main_end);
   if (e != hipSuccess) return e;
-  if (main_end && (e = hipEventRecord(main_end, stream)) != hipSuccess) return e;
+  if (main_end && !both && (e = hipEventRecord(main_end, stream)) != hipSuccess) return e;
   if (a.num_splits > 1) {
     hipLaunchKernelGGL(mla_combine_kernel, dim3(a.batch * a.row_groups * kCombineChunks), dim3(kCombineThreads),
                        0, stream, a);
