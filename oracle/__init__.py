@@ -18,3 +18,4 @@ from .mla_oracle import (  # noqa: F401
     merge_partials,
     resolve,
 )
+from .kv_append import FP8_MAX, append_kv, e4m3fn_round, quantize_row  # noqa: F401

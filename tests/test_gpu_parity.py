@@ -77,6 +77,17 @@ def test_causal_four_queries_layer_select(gpu_device):
     check_gate(run_gpu(w), oracle_decode(w), "causal q4")
 
 
+@pytest.mark.parametrize("q_len,heads,gran", [(16, 128, 64), (64, 16, 576)])
+def test_longer_query_runs(gpu_device, q_len, heads, gran):
+    """Chunked-prefill shapes (q_len >> 4) over the paged cache: many row
+    groups, each query position with its own causal limit."""
+    say("q_len", q_len, "heads", heads, "gran", gran)
+    w = _w(gpu_device, 3, heads, [q_len, 300, 1000], 64, gran, q_len=q_len,
+           independent_scales=gran == 64, spare_blocks=2, spare_scale_blocks=2, seed=43 + q_len,
+           poison=True)
+    check_gate(run_gpu(w), oracle_decode(w), f"q{q_len} h{heads}")
+
+
 def test_rows_mixing_query_positions(gpu_device):
     """16 heads x 4 queries: one 32-row group holds two query positions."""
     say("H=16, q_len 4")
