@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MLA_PAGED_ABI_VERSION 1
+#define MLA_PAGED_ABI_VERSION 2
 
 /* Status codes.  mla_status_string() returns a static description. */
 typedef enum {
@@ -156,6 +156,42 @@ mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, cons
                                          size_t workspace_bytes, int32_t num_splits,
                                          hipEvent_t main_begin, hipEvent_t main_end,
                                          hipStream_t stream);
+
+/*
+ * mla_append_kv_fp8 — write the latent rows of the q_len new tokens of every
+ * request into the paged FP8 cache, quantised; the step before a decode call.
+ * Storage as on the "generic_get_paged_cache_with_scales" page (section
+ * "Args"), scale type and granularity as on the "KVCacheScalesMHAOperand"
+ * page: new row i of request b is token t = cache_lengths[b] - q_len + i
+ * (cache_lengths already count the new tokens, as for decode); its codes go
+ * to blocks[LT[b, t / P], 0, layer_idx, t % P, 0, :] and its scales to
+ * scales[SLT[b, t / P], 0, layer_idx, t % P, 0, :] (SLT = LT when NULL).
+ *
+ * Quantisation per granularity group (576 / scale_groups elements): s =
+ * amax / 448 in float32 (correctly rounded), code = the E4M3FN value nearest
+ * to clip(x / s, -448, 448) with the division correctly rounded in float32,
+ * ties to the even code, the sign bit from x / s; a group whose amax is 0
+ * gets s = 0 and codes 0x00.
+ *
+ *   kv_new        bf16 [B, q_len, 576] (device, read)
+ *   blocks        E4M3FN bytes [num_blocks, kv_dim, num_layers, P, 1, 576] (written in place)
+ *   scales        float32 [num_scale_blocks, kv_dim, num_layers, P, 1, scale_groups] (written in place)
+ *   lookup_table, scales_lookup_table (or NULL), cache_lengths: as for decode
+ *   layer_idx     layer written, 0 <= layer_idx < num_layers
+ *   q_len         new tokens per request, >= 1
+ *   shape         the same shape description decode takes (num_q_heads is not used but must be > 0)
+ *
+ * Rows with t < 0 or t >= max_pages * page_size, and rows whose page id is
+ * >= num_blocks or whose scale page id is >= num_scale_blocks, are not
+ * written.  Only the row's 576 code bytes and scale_groups scales are
+ * written; everything else is left as it was.  Non-finite inputs are outside
+ * the contract.  Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_RANGE,
+ * MLA_ERR_UNSUPPORTED (as for decode), MLA_ERR_HIP (launch failed).
+ */
+mla_status mla_append_kv_fp8(const void* kv_new, void* blocks, float* scales,
+                             const uint32_t* lookup_table, const uint32_t* scales_lookup_table,
+                             const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                             const mla_shape* shape, hipStream_t stream);
 
 /* The decomposition a call with these sizes would use (host only, no HIP call
  * except a cached device-property query).  num_splits = 0 asks for the

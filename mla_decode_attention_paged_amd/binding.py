@@ -84,6 +84,9 @@ def load_library() -> ctypes.CDLL:
     lib.mla_decode_paged_fp8_plan.argtypes = [ctypes.POINTER(MlaShape), ctypes.c_int32, ctypes.c_int32,
                                               ctypes.POINTER(MlaPlan)]
     lib.mla_decode_paged_fp8_plan.restype = ctypes.c_int
+    lib.mla_append_kv_fp8.argtypes = [vp, vp, f32p, u32p, u32p, u32p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(MlaShape), vp]
+    lib.mla_append_kv_fp8.restype = ctypes.c_int
     lib.mla_resolve_pages.argtypes = [u32p, u32p, u32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, u32p, u32p, u32p, vp]
     lib.mla_resolve_pages.restype = ctypes.c_int
@@ -219,6 +222,42 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
     if st != MLA_OK:
         raise MlaError(st, "mla_decode_paged_fp8")
     return out
+
+
+def mla_append_kv_fp8(kv_new, blocks, scales, lookup_table, scales_lookup_table, cache_lengths,
+                      layer_idx, q_len, num_q_heads=128):
+    """Quantise the latent rows of the q_len new tokens of every request into the paged
+    FP8 cache, in place (blocks and scales are written); returns (blocks, scales).
+
+    kv_new bf16 [B, q_len, 576]; blocks uint8 (E4M3FN bytes) [NB, KVD, NL, P, 1, 576];
+    scales float32 [NBs, KVD, NL, P, 1, 576 / granularity]; tables and cache_lengths as
+    for mla_decode_paged_fp8 (cache_lengths count the new tokens).  num_q_heads only
+    fills the shape description the library validates.
+    """
+    lib = load_library()
+    dev = kv_new.device
+    if dev.type != "cuda":
+        raise ValueError("mla_append_kv_fp8 runs on the GPU only; got tensors on " + str(dev))
+    _check_tensor("kv_new", kv_new, (torch.bfloat16,), 3, dev)
+    _check_tensor("blocks", blocks, (torch.uint8, torch.float8_e4m3fn), 6, dev)
+    _check_tensor("scales", scales, (torch.float32,), 6, dev)
+    _check_tensor("lookup_table", lookup_table, (torch.int32,), 2, dev)
+    if scales_lookup_table is not None:
+        _check_tensor("scales_lookup_table", scales_lookup_table, (torch.int32,), 2, dev)
+    _check_tensor("cache_lengths", cache_lengths, (torch.int32,), 1, dev)
+    B, Q, D = kv_new.shape
+    if Q != q_len or D != blocks.shape[-1] or lookup_table.shape[0] != B or cache_lengths.shape[0] != B:
+        raise ValueError("mla_append_kv_fp8: kv_new, tables and cache_lengths disagree on batch / q_len / depth")
+    NB, KVD, NL, P, HKV, _ = blocks.shape
+    shp = MlaShape(batch=B, num_q_heads=int(num_q_heads), head_dim=D, v_dim=512, num_blocks=NB, kv_dim=KVD,
+                   num_layers=NL, page_size=P, num_kv_heads=HKV, num_scale_blocks=scales.shape[0],
+                   scale_groups=scales.shape[-1], max_pages=lookup_table.shape[1])
+    st = lib.mla_append_kv_fp8(_ptr(kv_new), _ptr(blocks), _ptr(scales), _ptr(lookup_table),
+                               _ptr(scales_lookup_table), _ptr(cache_lengths), int(layer_idx), int(q_len),
+                               ctypes.byref(shp), _stream_handle(dev))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_append_kv_fp8")
+    return blocks, scales
 
 
 def mla_resolve_pages(lookup_table, scales_lookup_table, cache_lengths, page_size, max_tokens):

@@ -184,6 +184,37 @@ mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, cons
                      num_splits > 0, stream, main_begin, main_end);
 }
 
+mla_status mla_append_kv_fp8(const void* kv_new, void* blocks, float* scales,
+                             const uint32_t* lookup_table, const uint32_t* scales_lookup_table,
+                             const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                             const mla_shape* shape, hipStream_t stream) {
+  if (!kv_new || !blocks || !scales || !lookup_table || !cache_lengths || !shape) return MLA_ERR_NULL;
+  mla_status st = check_shape(shape, q_len);
+  if (st != MLA_OK) return st;
+  if (layer_idx < 0 || layer_idx >= shape->num_layers) return MLA_ERR_RANGE;
+  if ((int64_t)shape->batch * q_len > ((int64_t)1 << 30)) return MLA_ERR_UNSUPPORTED;
+  mla::AppendArgs a{};
+  a.kv_new = (const uint16_t*)kv_new;
+  a.blocks = (uint8_t*)blocks;
+  a.scales = scales;
+  a.lt = lookup_table;
+  a.slt = scales_lookup_table ? scales_lookup_table : lookup_table;
+  a.cache_lengths = cache_lengths;
+  const int64_t P = shape->page_size;
+  a.page_stride = (int64_t)shape->kv_dim * shape->num_layers * P * shape->head_dim;
+  a.layer_offset = (int64_t)layer_idx * P * shape->head_dim;
+  a.spage_stride = (int64_t)shape->kv_dim * shape->num_layers * P * shape->scale_groups;
+  a.slayer_offset = (int64_t)layer_idx * P * shape->scale_groups;
+  a.num_blocks = shape->num_blocks;
+  a.num_scale_blocks = shape->num_scale_blocks;
+  a.batch = shape->batch;
+  a.q_len = q_len;
+  a.max_pages = shape->max_pages;
+  a.page_size = shape->page_size;
+  hipError_t e = mla::launch_append(a, shape->scale_groups, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 mla_status mla_decode_paged_fp8_plan(const mla_shape* shape, int32_t q_len, int32_t num_splits,
                                      mla_plan* plan) {
   if (!shape || !plan) return MLA_ERR_NULL;

@@ -43,6 +43,22 @@ struct DecodeArgs {
 
 size_t partial_bytes(int64_t batch, int64_t row_groups, int64_t num_splits);
 
+// Arguments of the append-and-quantise kernel (kv_append.hip).
+struct AppendArgs {
+  const uint16_t* kv_new;            // bf16 bits [B, Q, 576]: latent rows of the new tokens
+  uint8_t* blocks;                   // e4m3fn bytes, written
+  float* scales;                     // written
+  const uint32_t* lt;                // [B, max_pages]
+  const uint32_t* slt;               // scale page table; == lt when absent
+  const uint32_t* cache_lengths;     // [B], the new tokens included
+  int64_t page_stride, layer_offset; // bytes, as in DecodeArgs
+  int64_t spage_stride, slayer_offset;   // floats, as in DecodeArgs
+  int64_t num_blocks, num_scale_blocks;  // page ids at or past these are not written
+  int32_t batch, q_len, max_pages, page_size;
+};
+
+hipError_t launch_append(const AppendArgs& a, int scale_groups, hipStream_t stream);
+
 // Launch the decode kernel (and the split combine when num_splits > 1).  The
 // optional events are recorded right before / after the decode kernel.
 hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stream,

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert binding.mla_abi_version() == 1
+    assert binding.mla_abi_version() == 2
     for code in range(7):
         assert lib.mla_status_string(code).decode()
     assert lib.mla_status_string(99).decode() == "unknown status"
@@ -131,3 +131,27 @@ def test_resolve_rejects_bad_args(lib):
     assert lib.mla_resolve_pages(None, None, f, 2, 4, 16, 64, f, f, f, None) == NULL
     assert lib.mla_resolve_pages(f, None, f, 0, 4, 16, 64, f, f, f, None) == SHAPE
     assert lib.mla_resolve_pages(f, None, f, 2, 4, 16, 0, f, f, f, None) == SHAPE
+
+
+def call_append(lib, shape, *, layer=0, q_len=1, nulls=()):
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(5)]
+    for i in nulls:
+        fake[i] = None
+    kv, blocks, scales, lt, cl = fake
+    return lib.mla_append_kv_fp8(kv, blocks, scales, lt, None, cl, layer, q_len,
+                                 ctypes.byref(shape) if shape is not None else None, None)
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_append_null_pointers_rejected(lib, idx):
+    assert call_append(lib, good_shape(), nulls=(idx,)) == NULL
+
+
+@pytest.mark.parametrize("kw,shape_kw,code", [
+    (dict(layer=1), {}, RANGE), (dict(layer=-1), {}, RANGE), (dict(q_len=0), {}, RANGE),
+    ({}, dict(batch=0), SHAPE), ({}, dict(scale_groups=5), SHAPE), ({}, dict(scale_groups=3), UNSUP),
+    ({}, dict(head_dim=512), UNSUP), ({}, dict(page_size=24), UNSUP),
+])
+def test_append_bad_arguments_rejected(lib, kw, shape_kw, code):
+    assert call_append(lib, good_shape(**shape_kw), **kw) == code
+    assert call_append(lib, None) == NULL
