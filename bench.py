@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA16_TFLOPS = 2500.0      # MI355X dense FP16/BF16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 MALL_BYTES = 256 << 20
-WORKLOADS = ("uniform", "ragged", "long1", "long4", "spec", "tiny")
+WORKLOADS = ("uniform", "ragged", "long1", "long4", "spec", "chunk", "tiny")
 KERNEL_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "mla_decode.hip")
 
 # HBM traffic of one main-kernel launch, from two rocprofv3 --pmc runs of
@@ -66,6 +66,8 @@ def make(name, device):
         return synth.long_context(device=device, batch=4)
     if name == "spec":
         return synth.speculative(device=device)
+    if name == "chunk":
+        return synth.query_chunk(device=device)
     if name == "tiny":
         return synth.tiny(device=device, poison=False)
     raise ValueError(name)
@@ -192,6 +194,51 @@ def cpu_baseline(w):
                       f"{dt:.1f} s wall"}
 
 
+def bench_append(args, w):
+    """Time the append-and-quantize kernel on the workload's shape (B requests x q_len new rows)."""
+    import torch
+    from mla_decode_attention_paged_amd import mla_append_kv_fp8
+    dev = w.q.device
+    B, Q = w.batch, w.q_len
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    kv = (torch.randn((B, Q, 576), generator=g, device=dev) *
+          torch.exp(0.5 * torch.randn((B, Q, 1), generator=g, device=dev))).to(torch.bfloat16)
+    NG = w.scales.shape[-1]
+    tables = 1 if w.scales_lookup_table is None else 2
+    alg_bytes = B * Q * (576 * 2 + 576 + 4 * NG + 4 * tables) + 4 * B
+
+    def call():
+        mla_append_kv_fp8(kv, w.blocks, w.scales, w.lookup_table, w.scales_lookup_table, w.cache_lengths,
+                          w.layer_idx, Q)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+    log(f"bench append: {kern_ms * 1e3:.2f} us/launch, {gbs:.1f} GB/s algorithmic ({alg_bytes} B)")
+    print(json.dumps({
+        "metric": "KV append + quantize (paged FP8), 1 MI355X", "value": B * Q / (kern_ms * 1e-3),
+        "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16-in/fp8e4m3+fp32-scales-out", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_len": Q, "granularity": w.granularity,
+                   "page_size": w.page_size},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "mla_append_kernel",
+                     "kernel_avg_us": kern_ms * 1e3, "alg_bytes_per_launch": alg_bytes},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +247,9 @@ def main():
     ap.add_argument("--workload", default="uniform", choices=WORKLOADS)
     ap.add_argument("--splits", type=int, default=None, help="explicit split count (default: library plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="decode", choices=("decode", "append"),
+                    help="decode (default, the headline line) or append: the KV append-and-quantize "
+                         "kernel for the workload's q_len new tokens per request")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -217,6 +267,9 @@ def main():
     dev = torch.device("cuda:0")
     log(f"bench: workload {args.workload}, library {lib_path()}")
     w = make(args.workload, dev)
+    if args.op == "append":
+        bench_append(args, w)
+        return
     w, layers = replicate_layers(w, 2 * MALL_BYTES)
     alg_bytes, alg_flops, kv_tokens = algorithmic(w)
     plan = mla_decode_paged_fp8_plan(tuple(w.q.shape), tuple(w.blocks.shape), tuple(w.scales.shape),

@@ -219,3 +219,10 @@ def speculative(seed=4000, device="cpu", poison=False, batch=128, lmin=2048, lma
                          independent_scales=True, spare_blocks=5, spare_scale_blocks=9,
                          max_pages=(lmax + 63) // 64, seed=seed, device=device, poison=poison,
                          name=f"spec_b{batch}")
+
+
+def query_chunk(seed=5000, device="cpu", poison=False, batch=8, q_len=16, length=4096):
+    """batch x q_len 16 new tokens (causal) over 4096 cached keys, 128 heads, page 64,
+    per-token scales: a chunked-prefill shape over the paged cache."""
+    return make_workload(batch, 128, [length] * batch, 64, HEAD_DIM, q_len=q_len, seed=seed, device=device,
+                         poison=poison, name=f"chunk_b{batch}_q{q_len}_l{length}")
