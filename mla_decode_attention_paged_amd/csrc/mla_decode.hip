@@ -421,7 +421,7 @@ mla_decode_kernel(DecodeArgs a) {
     // The two tile-parity waves of a depth half need the same q: each loads its
     // own row group's share from HBM and passes it to the other through LDS
     // (staged in the tile buffers of steps 1 and 2, which are not loaded yet).
-    bf16x8 qv[2][18], qown[18];
+    bf16x8 qk[18], qg[18], qown[18];   // q of the row group this wave keeps (d) / gives (1 - d)
     {
       const int row = (2 * rgp + par) * kRows + n;
       const bool ok = row < rows_total;
@@ -443,8 +443,8 @@ mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 18; ++j) {
       const bf16x8 other = *(LDS_AS const bf16x8*)(qstage + (((d * 2 + (par ^ 1)) * 18 + j) * 64 + lane) * 16);
-      qv[0][j] = par ? other : qown[j];
-      qv[1][j] = par ? qown[j] : other;
+      qk[j] = par == d ? qown[j] : other;
+      qg[j] = par == d ? other : qown[j];
     }
     __syncthreads();            // step 0 has landed (the value waves waited for their loads)
 
@@ -454,9 +454,12 @@ mla_decode_kernel(DecodeArgs a) {
       const int t0 = t_lo + kTile * j;
       LDS_AS const char* tb = tile_buf(i, par);
       LDS_AS const char* sb = scale_buf(i, par);
-      // ---- phase 1: partial scores of both row groups over depth half d
-      f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+      // ---- phase 1: partial scores of both row groups over depth half d:
+      // accK for row group d (finished here), accG for row group 1 - d
+      f32x16 accK, accG;
       if (have) {
+        accK = f32x16{};
+        accG = f32x16{};
         // all nine key reads are issued up front: one LDS latency per tile (the
         // group-scale variant, short of registers, reads them as it goes)
         u32x4 kws[9];
@@ -471,44 +474,42 @@ mla_decode_kernel(DecodeArgs a) {
           const bf16x8 k0 = fp8x8_to_bf16(kw[0], kw[1]);
           const bf16x8 k1 = fp8x8_to_bf16(kw[2], kw[3]);
           if constexpr (NG == 1) {
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv[0][2 * s], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv[1][2 * s], acc1, 0, 0, 0);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv[0][2 * s + 1], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv[1][2 * s + 1], acc1, 0, 0, 0);
+            accK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qk[2 * s], accK, 0, 0, 0);
+            accG = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qg[2 * s], accG, 0, 0, 0);
+            accK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qk[2 * s + 1], accK, 0, 0, 0);
+            accG = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qg[2 * s + 1], accG, 0, 0, 0);
           } else {
             // block s is scale group s: acc += scale * (this half's partial sums)
             f32x16 u0 = f32x16{}, u1 = f32x16{};
-            u0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv[0][2 * s], u0, 0, 0, 0);
-            u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv[1][2 * s], u1, 0, 0, 0);
-            u0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv[0][2 * s + 1], u0, 0, 0, 0);
-            u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv[1][2 * s + 1], u1, 0, 0, 0);
+            u0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qk[2 * s], u0, 0, 0, 0);
+            u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qg[2 * s], u1, 0, 0, 0);
+            u0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qk[2 * s + 1], u0, 0, 0, 0);
+            u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qg[2 * s + 1], u1, 0, 0, 0);
             float sv16[16];
             lane_scales(sb, s, sv16);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              acc0[r] = __builtin_fmaf(sv16[r], u0[r], acc0[r]);
-              acc1[r] = __builtin_fmaf(sv16[r], u1[r], acc1[r]);
+              accK[r] = __builtin_fmaf(sv16[r], u0[r], accK[r]);
+              accG[r] = __builtin_fmaf(sv16[r], u1[r], accG[r]);
             }
           }
         }
         // the other row group's partial goes to the wave finishing it (same tile, depth 1 - d)
         LDS_AS char* xo = x_buf(i, par, d ^ 1);
-        const f32x16& give = d ? acc0 : acc1;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
-          *(LDS_AS f32x4*)(xo + 1024 * qq + 16 * lane) = f32x4{give[4 * qq], give[4 * qq + 1], give[4 * qq + 2], give[4 * qq + 3]};
+          *(LDS_AS f32x4*)(xo + 1024 * qq + 16 * lane) = f32x4{accG[4 * qq], accG[4 * qq + 1], accG[4 * qq + 2], accG[4 * qq + 3]};
       }
       lds_barrier();            // mid-step: partial scores exchanged
       // ---- phase 2: row group d of this tile: full scores, online softmax, P'
       if (have) {
         LDS_AS const char* xi = x_buf(i, par, d);
-        const f32x16& keep = d ? acc1 : acc0;
         float x[16];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const f32x4 o4 = *(LDS_AS const f32x4*)(xi + 1024 * qq + 16 * lane);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * qq + e] = keep[4 * qq + e] + o4[e];
+          for (int e = 0; e < 4; ++e) x[4 * qq + e] = accK[4 * qq + e] + o4[e];
         }
         // x = the scaled score without softmax_scale (exponents use c2 * (x - m))
         float sv16[16];
