@@ -913,34 +913,46 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(DecodeArgs
   if (row >= rows_total) return;
 
   const size_t pbase = ((size_t)b * a.row_groups + rg) * a.num_splits;
-  float M = kNegInf;
-  for (int s = 0; s < nsplit_eff; ++s) M = fmaxf(M, a.ws_lse[(pbase + s) * kRows + rl]);
+  // Online over batches of eight splits: each batch's sixteen O loads and
+  // eight lse loads are in flight together; the running maximum M moves (and
+  // the sums are rescaled) only when a batch raises it.
+  float M = kNegInf, W = 0.0f;
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  float W = 0.0f;
-  if (M != kNegInf) {
-    // eight splits per batch: their sixteen loads are all in flight together
-    for (int s0 = 0; s0 < nsplit_eff; s0 += 8) {
-      f32x4 v[8][2];
-      float w[8];
+  for (int s0 = 0; s0 < nsplit_eff; s0 += 8) {
+    f32x4 v[8][2];
+    float ls[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int s = min(s0 + u, nsplit_eff - 1);
-        const float ls = a.ws_lse[(pbase + s) * kRows + rl];
-        w[u] = (s0 + u < nsplit_eff && ls != kNegInf) ? exp2_fast(ls - M) : 0.0f;
-        const f32x4* src = (const f32x4*)(a.ws_o + ((pbase + s) * kRows + rl) * kVDim + col0);
-        v[u][0] = src[0];
-        v[u][1] = src[1];
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, nsplit_eff - 1);
+      ls[u] = a.ws_lse[(pbase + s) * kRows + rl];
+      const f32x4* src = (const f32x4*)(a.ws_o + ((pbase + s) * kRows + rl) * kVDim + col0);
+      v[u][0] = src[0];
+      v[u][1] = src[1];
+    }
+    float mb = kNegInf;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        W += w[u];
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u >= nsplit_eff) ls[u] = kNegInf;     // (a repeated last split)
+      mb = fmaxf(mb, ls[u]);
+    }
+    if (mb > M) {
+      const float r = M == kNegInf ? 0.0f : exp2_fast(M - mb);
+      W *= r;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[j] = __builtin_fmaf(w[u], v[u][0][j], acc[j]);
-          acc[4 + j] = __builtin_fmaf(w[u], v[u][1][j], acc[4 + j]);
-        }
+      for (int j = 0; j < 8; ++j) acc[j] *= r;
+      M = mb;
+    }
+    if (M == kNegInf) continue;                      // nothing visible yet
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = ls[u] == kNegInf ? 0.0f : exp2_fast(ls[u] - M);
+      W += w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = __builtin_fmaf(w, v[u][0][j], acc[j]);
+        acc[4 + j] = __builtin_fmaf(w, v[u][1][j], acc[4 + j]);
       }
     }
   }
