@@ -409,8 +409,12 @@ mla_decode_kernel(DecodeArgs a) {
     // K read (A operand): lane (key n, half g) reads 16-byte column 4s + 2d + g
     // of its key for 64-byte block s.
     const uint32_t kread = (uint32_t)(1024 * 9 * (n >> 4) + 16 * (4 * (n & 15) + ((2 * d + g) ^ ((n >> 2) & 3))));
-    // lazy threshold: the reference moves when a score passes it by 8 / c2 (p <= 2^8)
-    const float thr = 8.0f / c2;
+    // Lazy threshold: the reference moves only when a score passes it by thr,
+    // so p <= 2^(c2 thr).  With group scales P' is formed on the value side and
+    // thr stays at 8 / c2 (p <= 2^8); with per-token scales it is set per tile
+    // so that P' = p * s stays below 2^15 (finite in f16) for the tile's largest
+    // scale, at most 16 / c2.
+    const float thr8 = 8.0f / c2;
 
     float m_run = kNegInf;     // running reference max per row (same in both halves), unscaled
     float l_part = 0.0f;       // this lane's share of the row sum, against m_run
@@ -513,10 +517,16 @@ mla_decode_kernel(DecodeArgs a) {
         }
         // x = the scaled score without softmax_scale (exponents use c2 * (x - m))
         float sv16[16];
+        float thr = thr8;
         if constexpr (NG == 1) {
           lane_scales(sb, 0, sv16);
 #pragma unroll
           for (int r = 0; r < 16; ++r) x[r] *= sv16[r];
+          float smax = sv16[0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) smax = fmaxf(smax, sv16[r]);
+          smax = halves_max(smax);                        // the tile's 32 keys
+          thr = fminf(16.0f, fmaxf(0.0f, 15.0f - __log2f(smax))) / c2;
         }
         if (t0 + kTile > lim_min) {
 #pragma unroll
@@ -626,8 +636,10 @@ mla_decode_kernel(DecodeArgs a) {
         LDS_AS float* mol = mo_lds + r * kRows;
         LDS_AS const float* a0 = alpha_buf(step, 0, r);
         LDS_AS const float* a1 = alpha_buf(step, 1, r);
+        // (while every row's reference is still -inf, O is zero: nothing to scale)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
+          if (!wave_any(mo_a[r] != kNegInf)) break;
           const f32x4 old = *(LDS_AS const f32x4*)(mol + 8 * qq + 4 * g);
           const f32x4 t0 = *(LDS_AS const f32x4*)(a0 + 8 * qq + 4 * g);
           const f32x4 t1 = two ? *(LDS_AS const f32x4*)(a1 + 8 * qq + 4 * g) : f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
