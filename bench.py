@@ -35,7 +35,7 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "mla_d
 # `bench.py --steps 5 --warmup 2 --no-cpu-baseline` (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch, averaged over the dispatches), each scaled by
 # what the same counter reads for a plain 1 GiB device copy
-# (`bench.py --calibrate-copy`: FETCH_SIZE 524,302.5 KiB and WRITE_SIZE
+# (`bench.py --calibrate-copy`: FETCH_SIZE 524,302.4 KiB and WRITE_SIZE
 # 1,048,576 KiB for 1,048,576 KiB moved).  The writes are the split partials
 # (workspace), not part of the algorithmic bytes.  Keyed by the SHA-256 of the
 # device code the counters were taken on (kernel_digest): any later edit of a
@@ -44,8 +44,8 @@ _COPY_KIB = 1048576.0
 _FETCH_PER_KIB = 524302.5 / _COPY_KIB
 _WRITE_PER_KIB = 1048576.0 / _COPY_KIB
 MEASURED_TRAFFIC = {
-    "8e7bc20e1701b4867cb667059d81c8943d7f944ddde96df6ee4a8394764ec941": {
-        "uniform_b16_l4096": {"fetch_kib": 19944.34, "write_kib": 33344.0},
+    "ef315dbc6813c2e77ba3ef4f9d64ff1ab96bafe38211a20c724c525dcb647706": {
+        "uniform_b16_l4096": {"fetch_kib": 19941.30, "write_kib": 32832.0},
     },
 }
 
