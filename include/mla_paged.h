@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MLA_PAGED_ABI_VERSION 2
+#define MLA_PAGED_ABI_VERSION 3
 
 /* Status codes.  mla_status_string() returns a static description. */
 typedef enum {
@@ -156,6 +156,47 @@ mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, cons
                                          size_t workspace_bytes, int32_t num_splits,
                                          hipEvent_t main_begin, hipEvent_t main_end,
                                          hipStream_t stream);
+
+/*
+ * mla_decode_paged_bf16 — the same attention over an unquantized paged cache.
+ *
+ * Quantization is a property of the cache type ("KVCacheScalesMHAOperand"
+ * page, the quantization_enabled alias); without it the latent rows are kept
+ * as they are, in the blocks tensor of "generic_get_paged_cache_with_scales"
+ * (section "Args"), here as bf16, and there are no scales:
+ *   K_j[d] = blocks[LT[b, j/P], 0, layer_idx, j%P, 0, d]
+ * and everything else (scores over the 576-deep row, V = K_j[0:512], the
+ * causal rule for q_len > 1, empty rows -> zeros) is as for
+ * mla_decode_paged_fp8.
+ *
+ *   q        bf16 [batch, q_len, num_q_heads, 576] (device, read)
+ *   blocks   bf16 [num_blocks, kv_dim, num_layers, page_size, 1, 576] (device, read)
+ *   lookup_table u32 [batch, max_pages], cache_lengths u32 [batch] (device, read)
+ *   out      bf16 [batch, q_len, num_q_heads, 512] (device, written)
+ *   shape    as for mla_decode_paged_fp8; num_scale_blocks and scale_groups
+ *            are not used (any value)
+ *   workspace / workspace_bytes: split partials, as for mla_decode_paged_fp8;
+ *            the plan (and so the size) is the one mla_decode_paged_fp8_plan
+ *            reports for the same shape and q_len.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_RANGE, MLA_ERR_UNSUPPORTED,
+ * MLA_ERR_HIP, as for mla_decode_paged_fp8.  The probabilities enter the
+ * value contraction as a sum of two bf16 numbers (about 16 significant bits).
+ */
+mla_status mla_decode_paged_bf16(const void* q, const void* blocks, const uint32_t* lookup_table,
+                                 const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                                 float softmax_scale, void* out, const mla_shape* shape,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* mla_decode_paged_bf16 with an explicit split count (0 = automatic; an
+ * explicit count needs plan.workspace_bytes of workspace) and the optional
+ * kernel-timing events of mla_decode_paged_fp8_profiled (NULL = none). */
+mla_status mla_decode_paged_bf16_profiled(const void* q, const void* blocks,
+                                          const uint32_t* lookup_table, const uint32_t* cache_lengths,
+                                          int32_t layer_idx, int32_t q_len, float softmax_scale,
+                                          void* out, const mla_shape* shape, void* workspace,
+                                          size_t workspace_bytes, int32_t num_splits,
+                                          hipEvent_t main_begin, hipEvent_t main_end,
+                                          hipStream_t stream);
 
 /*
  * mla_append_kv_fp8 — write the latent rows of the q_len new tokens of every

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     load_library,
     mla_abi_version,
     mla_append_kv_fp8,
+    mla_decode_paged_bf16,
     mla_decode_paged_fp8,
     mla_decode_paged_fp8_plan,
     mla_resolve_pages,

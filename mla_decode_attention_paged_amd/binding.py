@@ -81,6 +81,12 @@ def load_library() -> ctypes.CDLL:
     lib.mla_decode_paged_fp8_splits.restype = ctypes.c_int
     lib.mla_decode_paged_fp8_profiled.argtypes = common + [ctypes.c_int32, vp, vp, vp]
     lib.mla_decode_paged_fp8_profiled.restype = ctypes.c_int
+    bf16_common = [vp, vp, u32p, u32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp,
+                   ctypes.POINTER(MlaShape), vp, ctypes.c_size_t]
+    lib.mla_decode_paged_bf16.argtypes = bf16_common + [vp]
+    lib.mla_decode_paged_bf16.restype = ctypes.c_int
+    lib.mla_decode_paged_bf16_profiled.argtypes = bf16_common + [ctypes.c_int32, vp, vp, vp]
+    lib.mla_decode_paged_bf16_profiled.restype = ctypes.c_int
     lib.mla_decode_paged_fp8_plan.argtypes = [ctypes.POINTER(MlaShape), ctypes.c_int32, ctypes.c_int32,
                                               ctypes.POINTER(MlaPlan)]
     lib.mla_decode_paged_fp8_plan.restype = ctypes.c_int
@@ -221,6 +227,57 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
         st = lib.mla_decode_paged_fp8_splits(*args, int(num_splits), _stream_handle(dev))
     if st != MLA_OK:
         raise MlaError(st, "mla_decode_paged_fp8")
+    return out
+
+
+def mla_decode_paged_bf16(q, blocks, lookup_table, cache_lengths, layer_idx, q_len, softmax_scale,
+                          out=None, workspace=None, num_splits=None, main_events=None):
+    """Decode attention over an unquantized paged cache; returns `out` (bf16 [B, q_len, H, 512]).
+
+    q bf16 [B, q_len, H, 576]; blocks bf16 [NB, KVD, NL, P, 1, 576];
+    lookup_table uint32 ids in an int32 tensor [B, max_pages]; cache_lengths
+    uint32 in an int32 tensor [B].  workspace, num_splits and main_events as
+    for mla_decode_paged_fp8 (the split plan is the same).
+    """
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("mla_decode_paged_bf16 runs on the GPU only; got tensors on " + str(dev))
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], q.shape[2], 512), dtype=torch.bfloat16, device=dev)
+    _check_tensor("q", q, (torch.bfloat16,), 4, dev)
+    _check_tensor("blocks", blocks, (torch.bfloat16,), 6, dev)
+    _check_tensor("lookup_table", lookup_table, (torch.int32,), 2, dev)
+    _check_tensor("cache_lengths", cache_lengths, (torch.int32,), 1, dev)
+    _check_tensor("out", out, (torch.bfloat16,), 4, dev)
+    B = q.shape[0]
+    if blocks.shape[5] != q.shape[3]:
+        raise ValueError("head_dim of q and blocks differ")
+    if lookup_table.shape[0] != B or cache_lengths.shape[0] != B:
+        raise ValueError("lookup_table / cache_lengths batch size differs from q")
+    if tuple(out.shape) != (B, q.shape[1], q.shape[2], 512):
+        raise ValueError(f"out must be [B, q_len, H, 512], got {tuple(out.shape)}")
+    NB, KVD, NL, P, HKV, D = blocks.shape
+    shp = MlaShape(batch=B, num_q_heads=q.shape[2], head_dim=q.shape[3], v_dim=512, num_blocks=NB,
+                   kv_dim=KVD, num_layers=NL, page_size=P, num_kv_heads=HKV, num_scale_blocks=1,
+                   scale_groups=1, max_pages=lookup_table.shape[1])
+    want = 0 if num_splits is None else int(num_splits)
+    if workspace is None:
+        need = mla_decode_paged_fp8_plan(tuple(q.shape), tuple(blocks.shape), (1, KVD, NL, P, HKV, 1),
+                                         tuple(lookup_table.shape), q_len, want)["workspace_bytes"]
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(q), _ptr(blocks), _ptr(lookup_table), _ptr(cache_lengths), int(layer_idx), int(q_len),
+            float(softmax_scale), _ptr(out), ctypes.byref(shp), ws_ptr, ws_bytes)
+    if main_events is not None or num_splits is not None:
+        ev = main_events if main_events is not None else (None, None)
+        st = lib.mla_decode_paged_bf16_profiled(*args, want, ctypes.c_void_p(ev[0]), ctypes.c_void_p(ev[1]),
+                                                _stream_handle(dev))
+    else:
+        st = lib.mla_decode_paged_bf16(*args, _stream_handle(dev))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_decode_paged_bf16")
     return out
 
 

@@ -85,16 +85,27 @@ mla_status make_plan(const mla_shape* s, int32_t q_len, int32_t want_splits, siz
   return MLA_OK;
 }
 
+// Shape check of an unquantized (bf16) cache: the scale fields do not apply.
+mla_status check_shape_unquantized(const mla_shape* s, int32_t q_len) {
+  if (!s) return MLA_ERR_NULL;
+  mla_shape t = *s;
+  t.num_scale_blocks = 1;
+  t.scale_groups = 1;
+  return check_shape(&t, q_len);
+}
+
+// unquantized: blocks hold bf16 rows and there are no scales (scales and
+// scales_lookup_table are ignored).
 mla_status decode_impl(const void* q, const void* blocks, const float* scales,
                        const uint32_t* lookup_table, const uint32_t* scales_lookup_table,
                        const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
                        float softmax_scale, void* out, const mla_shape* shape, void* workspace,
                        size_t workspace_bytes, int32_t num_splits, bool explicit_splits,
                        hipStream_t stream, hipEvent_t main_begin = nullptr,
-                       hipEvent_t main_end = nullptr) {
-  if (!q || !blocks || !scales || !lookup_table || !cache_lengths || !out || !shape)
+                       hipEvent_t main_end = nullptr, bool unquantized = false) {
+  if (!q || !blocks || (!unquantized && !scales) || !lookup_table || !cache_lengths || !out || !shape)
     return MLA_ERR_NULL;
-  mla_status st = check_shape(shape, q_len);
+  mla_status st = unquantized ? check_shape_unquantized(shape, q_len) : check_shape(shape, q_len);
   if (st != MLA_OK) return st;
   if (layer_idx < 0 || layer_idx >= shape->num_layers) return MLA_ERR_RANGE;
   if (num_splits < 0) return MLA_ERR_RANGE;
@@ -116,19 +127,22 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
   mla::DecodeArgs a{};
   a.q = (const uint16_t*)q;
   a.blocks = (const uint8_t*)blocks;
-  a.scales = scales;
+  a.scales = unquantized ? nullptr : scales;
   a.lt = lookup_table;
-  a.slt = scales_lookup_table ? scales_lookup_table : lookup_table;
+  a.slt = (!unquantized && scales_lookup_table) ? scales_lookup_table : lookup_table;
   a.cache_lengths = cache_lengths;
   a.out = (uint16_t*)out;
   const size_t units = (size_t)shape->batch * plan.row_groups * plan.num_splits;
   a.ws_o = plan.num_splits > 1 ? (float*)workspace : nullptr;
   a.ws_lse = plan.num_splits > 1 ? (float*)workspace + units * kRows * mla::kVDim : nullptr;
   const int64_t P = shape->page_size;
-  a.page_stride = (int64_t)shape->kv_dim * shape->num_layers * P * shape->head_dim;
-  a.layer_offset = (int64_t)layer_idx * P * shape->head_dim;
-  a.spage_stride = (int64_t)shape->kv_dim * shape->num_layers * P * shape->scale_groups;
-  a.slayer_offset = (int64_t)layer_idx * P * shape->scale_groups;
+  const int64_t elem = unquantized ? 2 : 1;     // bytes per cached element
+  a.page_stride = (int64_t)shape->kv_dim * shape->num_layers * P * shape->head_dim * elem;
+  a.layer_offset = (int64_t)layer_idx * P * shape->head_dim * elem;
+  if (!unquantized) {
+    a.spage_stride = (int64_t)shape->kv_dim * shape->num_layers * P * shape->scale_groups;
+    a.slayer_offset = (int64_t)layer_idx * P * shape->scale_groups;
+  }
   a.batch = shape->batch;
   a.q_len = q_len;
   a.num_heads = shape->num_q_heads;
@@ -140,7 +154,8 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
   a.grid_units = (int32_t)((size_t)shape->batch * ((plan.row_groups + 1) / 2) * plan.num_splits);
   a.sm_log2 = softmax_scale * 1.4426950408889634f;
 
-  hipError_t e = mla::launch_decode(a, shape->scale_groups, stream, main_begin, main_end);
+  hipError_t e = unquantized ? mla::launch_decode_bf16(a, stream, main_begin, main_end)
+                             : mla::launch_decode(a, shape->scale_groups, stream, main_begin, main_end);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -182,6 +197,27 @@ mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, cons
   return decode_impl(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
                      q_len, softmax_scale, out, shape, workspace, workspace_bytes, num_splits,
                      num_splits > 0, stream, main_begin, main_end);
+}
+
+mla_status mla_decode_paged_bf16(const void* q, const void* blocks, const uint32_t* lookup_table,
+                                 const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                                 float softmax_scale, void* out, const mla_shape* shape,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(q, blocks, nullptr, lookup_table, nullptr, cache_lengths, layer_idx, q_len,
+                     softmax_scale, out, shape, workspace, workspace_bytes, 0, false, stream, nullptr,
+                     nullptr, true);
+}
+
+mla_status mla_decode_paged_bf16_profiled(const void* q, const void* blocks,
+                                          const uint32_t* lookup_table, const uint32_t* cache_lengths,
+                                          int32_t layer_idx, int32_t q_len, float softmax_scale,
+                                          void* out, const mla_shape* shape, void* workspace,
+                                          size_t workspace_bytes, int32_t num_splits,
+                                          hipEvent_t main_begin, hipEvent_t main_end,
+                                          hipStream_t stream) {
+  return decode_impl(q, blocks, nullptr, lookup_table, nullptr, cache_lengths, layer_idx, q_len,
+                     softmax_scale, out, shape, workspace, workspace_bytes, num_splits,
+                     num_splits > 0, stream, main_begin, main_end, true);
 }
 
 mla_status mla_append_kv_fp8(const void* kv_new, void* blocks, float* scales,

@@ -1034,12 +1034,14 @@ hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stre
                         : launch_main<9>(a, stream, main_begin, main_end);
   if (e != hipSuccess) return e;
   if (main_end && !both && (e = hipEventRecord(main_end, stream)) != hipSuccess) return e;
-  if (a.num_splits > 1) {
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(a.batch * a.row_groups * kCombineChunks), dim3(kCombineThreads),
-                       0, stream, a);
-    e = hipGetLastError();
-  }
+  if (a.num_splits > 1) e = launch_combine(a, stream);
   return e;
+}
+
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(a.batch * a.row_groups * kCombineChunks), dim3(kCombineThreads),
+                     0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_resolve(const uint32_t* lt, const uint32_t* slt, const uint32_t* cache_lengths,

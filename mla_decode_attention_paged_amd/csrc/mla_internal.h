@@ -64,6 +64,16 @@ hipError_t launch_append(const AppendArgs& a, int scale_groups, hipStream_t stre
 hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stream,
                          hipEvent_t main_begin = nullptr, hipEvent_t main_end = nullptr);
 
+// Launch the unquantized (bf16 cache) decode kernel, then the split combine
+// when num_splits > 1.  DecodeArgs as for the FP8 kernel with blocks holding
+// bf16 rows (page_stride / layer_offset in bytes); scales and slt are unused.
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin = nullptr,
+                              hipEvent_t main_end = nullptr);
+
+// The split combine alone (mla_decode.hip): merges the fp32 partials in a.ws_o /
+// a.ws_lse into a.out.
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
+
 hipError_t launch_resolve(const uint32_t* lt, const uint32_t* slt, const uint32_t* cache_lengths,
                           int batch, int max_pages, int page_size, int max_tokens,
                           uint32_t* page, uint32_t* slot, uint32_t* spage, hipStream_t stream);

@@ -16,12 +16,14 @@ Value recipe (shared by all workloads):
   row    = N(0, 1)^576 * m,  m ~ LogNormal(0, 0.5)      per cached token
   scale  = float32(amax(|row_g|) / 448)                 per group g of `granularity`
   code   = e4m3fn(clip(row_g / scale, -448, 448))       round to nearest even
+With kv_dtype="bf16" (the unquantized cache) blocks holds bf16(row) and
+there are no scales.
 Page ids of a request are drawn from a random permutation of the pool, in
 (request, page) order; scale pages use their own permutation when the scales
 are paged independently.  Slots past a request's length, pages no request
 uses, layers other than the selected one and kv_dim entries other than 0 are
-filled with `fill_code` (0x7F, an E4M3FN NaN, in poison mode) so that any read
-of them shows up in the result.
+filled with `fill_code` (0x7F, an E4M3FN NaN, in poison mode; a bf16 NaN for
+the unquantized cache) so that any read of them shows up in the result.
 """
 
 from __future__ import annotations
@@ -43,8 +45,8 @@ class Workload:
     """One decode call's inputs (tensors live on `device`)."""
 
     q: torch.Tensor                  # bf16 [B, Q, H, 576]
-    blocks: torch.Tensor             # uint8 [NB, KVD, NL, P, 1, 576]
-    scales: torch.Tensor             # float32 [NBs, KVD, NL, P, 1, NG]
+    blocks: torch.Tensor             # uint8 [NB, KVD, NL, P, 1, 576] (bf16 when unquantized)
+    scales: torch.Tensor | None      # float32 [NBs, KVD, NL, P, 1, NG]; None when unquantized
     lookup_table: torch.Tensor       # int32 view of uint32 ids [B, max_pages]
     scales_lookup_table: torch.Tensor | None
     cache_lengths: torch.Tensor      # int32 view of uint32 [B]
@@ -92,7 +94,7 @@ def make_workload(batch, num_heads, cache_lengths, page_size, granularity, *, q_
                   num_layers=1, layer_idx=0, kv_dim=1, independent_scales=False,
                   spare_blocks=0, spare_scale_blocks=0, max_pages=None, seed=0,
                   softmax_scale=None, device="cpu", poison=True, unused_table_id=0,
-                  chunk_tokens=1 << 20, name=""):
+                  chunk_tokens=1 << 20, name="", kv_dtype="fp8"):
     """Draw one workload.
 
     cache_lengths: list of per-request lengths (each >= q_len unless a test
@@ -100,8 +102,16 @@ def make_workload(batch, num_heads, cache_lengths, page_size, granularity, *, q_
     page count.  With `poison`, every byte the decode must not read holds the
     NaN code 0x7F (NaN scales likewise); otherwise zeros.  unused_table_id is
     written into table columns past a request's pages (0xFFFFFFFF in poison
-    tests: such a column must never be read).
+    tests: such a column must never be read).  kv_dtype "bf16" draws the
+    unquantized cache: blocks hold the bf16 rows themselves, scales is None
+    (granularity and independent_scales do not apply).
     """
+    if kv_dtype not in ("fp8", "bf16"):
+        raise ValueError("kv_dtype is 'fp8' or 'bf16'")
+    unquantized = kv_dtype == "bf16"
+    if unquantized:
+        independent_scales = False
+        granularity = HEAD_DIM
     gen = torch.Generator(device="cpu")
     gen.manual_seed(int(seed))
     dgen = torch.Generator(device=device)
@@ -134,8 +144,15 @@ def make_workload(batch, num_heads, cache_lengths, page_size, granularity, *, q_
                 slt[b, c] = int(sperm[k])
             k += 1
 
-    blocks = torch.full((NB, kv_dim, num_layers, P, 1, HEAD_DIM), fill_code, dtype=torch.uint8, device=device)
-    scales = torch.full((NBs, kv_dim, num_layers, P, 1, NG), fill_scale, dtype=torch.float32, device=device)
+    if unquantized:
+        blocks = torch.full((NB, kv_dim, num_layers, P, 1, HEAD_DIM), float("nan") if poison else 0.0,
+                            dtype=torch.bfloat16, device=device)
+        scales = None
+    else:
+        blocks = torch.full((NB, kv_dim, num_layers, P, 1, HEAD_DIM), fill_code, dtype=torch.uint8,
+                            device=device)
+        scales = torch.full((NBs, kv_dim, num_layers, P, 1, NG), fill_scale, dtype=torch.float32,
+                            device=device)
 
     # latent rows of every valid token, drawn in chunks (large pools)
     tok_b = np.repeat(np.arange(B), lengths)
@@ -148,14 +165,17 @@ def make_workload(batch, num_heads, cache_lengths, page_size, granularity, *, q_
         n = s1 - s0
         rows = torch.randn((n, HEAD_DIM), generator=dgen, device=device, dtype=torch.float32)
         mag = torch.exp(0.5 * torch.randn((n, 1), generator=dgen, device=device, dtype=torch.float32))
-        codes, sc = _quantize_rows(rows * mag, granularity)
         bb = tok_b[s0:s1]
         tt = tok_t[s0:s1]
         page = torch.as_tensor(lt_np[bb, tt // P], device=device)
         spage = torch.as_tensor(slt_np[bb, tt // P], device=device)
         slot = torch.as_tensor(tt % P, device=device)
-        blocks[page, 0, layer_idx, slot, 0, :] = codes
-        scales[spage, 0, layer_idx, slot, 0, :] = sc
+        if unquantized:
+            blocks[page, 0, layer_idx, slot, 0, :] = (rows * mag).to(torch.bfloat16)
+        else:
+            codes, sc = _quantize_rows(rows * mag, granularity)
+            blocks[page, 0, layer_idx, slot, 0, :] = codes
+            scales[spage, 0, layer_idx, slot, 0, :] = sc
 
     q = torch.randn((B, q_len, num_heads, HEAD_DIM), generator=dgen, device=device,
                     dtype=torch.float32).to(torch.bfloat16)
@@ -226,3 +246,10 @@ def query_chunk(seed=5000, device="cpu", poison=False, batch=8, q_len=16, length
     per-token scales: a chunked-prefill shape over the paged cache."""
     return make_workload(batch, 128, [length] * batch, 64, HEAD_DIM, q_len=q_len, seed=seed, device=device,
                          poison=poison, name=f"chunk_b{batch}_q{q_len}_l{length}")
+
+
+def uniform_bf16(seed=6000, device="cpu", poison=False, batch=16, length=4096):
+    """The uniform shape (16 requests x 4096 keys, 128 heads, page 64) over an
+    unquantized bf16 cache."""
+    return make_workload(batch, 128, [length] * batch, 64, HEAD_DIM, seed=seed, device=device,
+                         poison=poison, kv_dtype="bf16", name=f"uniform_bf16_b{batch}_l{length}")

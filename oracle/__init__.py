@@ -19,3 +19,4 @@ from .mla_oracle import (  # noqa: F401
     resolve,
 )
 from .kv_append import FP8_MAX, append_kv, e4m3fn_round, quantize_row  # noqa: F401
+from .unquantized import decode_unquantized, gather_rows  # noqa: F401

@@ -60,7 +60,7 @@ def extract_requests(w, batches):
         pages, spages = [0], [0]
     dev = w.blocks.device
     blocks = w.blocks[torch.as_tensor(pages, device=dev)][:, :, :, :, :, :].contiguous()
-    scales = w.scales[torch.as_tensor(spages, device=dev)].contiguous()
+    scales = None if w.scales is None else w.scales[torch.as_tensor(spages, device=dev)].contiguous()
     return Workload(
         q=w.q[torch.as_tensor(batches, device=w.q.device)].contiguous(), blocks=blocks, scales=scales,
         lookup_table=_u32_view(torch.tensor(new_lt)).to(dev),

@@ -9,8 +9,10 @@ from mla_decode_attention_paged_amd.synth import u32_numpy
 def to_numpy(w):
     """(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths) as numpy."""
     q = w.q.detach().to("cpu").to(torch.float64).numpy()
-    blocks = w.blocks.detach().to("cpu").numpy()
-    scales = w.scales.detach().to("cpu").numpy()
+    blocks = w.blocks.detach().to("cpu")
+    # bf16 rows of an unquantized cache widen exactly to float64
+    blocks = blocks.to(torch.float64).numpy() if blocks.dtype == torch.bfloat16 else blocks.numpy()
+    scales = None if w.scales is None else w.scales.detach().to("cpu").numpy()
     lt = u32_numpy(w.lookup_table)
     slt = None if w.scales_lookup_table is None else u32_numpy(w.scales_lookup_table)
     cl = u32_numpy(w.cache_lengths)
@@ -22,6 +24,13 @@ def oracle_decode(w, batches=None, return_lse=False):
     q, blocks, scales, lt, slt, cl = to_numpy(w)
     return decode(q, blocks, scales, lt, slt, cl, w.layer_idx, w.q_len, w.softmax_scale,
                   batches=batches, return_lse=return_lse)
+
+
+def oracle_decode_unquantized(w, batches=None, return_lse=False):
+    from oracle import decode_unquantized
+    q, blocks, _, lt, _, cl = to_numpy(w)
+    return decode_unquantized(q, blocks, lt, cl, w.layer_idx, w.q_len, w.softmax_scale,
+                              batches=batches, return_lse=return_lse)
 
 
 def gate_stats(gpu, ref64):

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert binding.mla_abi_version() == 2
+    assert binding.mla_abi_version() == 3
     for code in range(7):
         assert lib.mla_status_string(code).decode()
     assert lib.mla_status_string(99).decode() == "unknown status"
@@ -155,3 +155,38 @@ def test_append_null_pointers_rejected(lib, idx):
 def test_append_bad_arguments_rejected(lib, kw, shape_kw, code):
     assert call_append(lib, good_shape(**shape_kw), **kw) == code
     assert call_append(lib, None) == NULL
+
+
+def call_bf16(lib, shape, *, layer=0, q_len=1, sm=0.07, nulls=()):
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(5)]
+    for i in nulls:
+        fake[i] = None
+    q, blocks, lt, cl, out = fake
+    return lib.mla_decode_paged_bf16(q, blocks, lt, cl, layer, q_len, ctypes.c_float(sm), out,
+                                     ctypes.byref(shape) if shape is not None else None, None, 0, None)
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_bf16_null_pointers_rejected(lib, idx):
+    assert call_bf16(lib, good_shape(), nulls=(idx,)) == NULL
+
+
+@pytest.mark.parametrize("kw,shape_kw,code", [
+    (dict(layer=1), {}, RANGE), (dict(q_len=0), {}, RANGE), (dict(sm=-1.0), {}, RANGE),
+    ({}, dict(batch=0), SHAPE), ({}, dict(head_dim=512), UNSUP), ({}, dict(page_size=24), UNSUP),
+    ({}, dict(num_kv_heads=2), UNSUP),
+])
+def test_bf16_bad_arguments_rejected(lib, kw, shape_kw, code):
+    assert call_bf16(lib, good_shape(**shape_kw), **kw) == code
+    assert call_bf16(lib, None) == NULL
+
+
+def test_bf16_ignores_scale_fields():
+    """The scale fields of the shape do not apply to an unquantized cache: values
+    that the FP8 entry rejects pass the host checks here (checked with a NULL q so
+    that nothing is launched)."""
+    lib = binding.load_library()
+    for kw in (dict(scale_groups=5), dict(scale_groups=0, num_scale_blocks=0)):
+        assert call(lib, good_shape(**kw)) in (SHAPE, UNSUP)
+        assert call_bf16(lib, good_shape(**kw), nulls=(0,)) == NULL
+        assert call_bf16(lib, good_shape(**kw), layer=5) == RANGE

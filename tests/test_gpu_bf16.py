@@ -1,0 +1,92 @@
+"""GPU parity of the unquantized (bf16 cache) decode, through the C ABI,
+against the FP64 oracle of oracle/unquantized.py.
+
+The gate is the one of the FP8 path: e = |gpu - bf16(oracle)| / max(1, |oracle|),
+max e <= 1e-2 and mean e <= 1e-3.  Cases cover NaN-poisoned unused slots,
+pages and layers, ragged tails around the 32-key tile and 16-key load block,
+lengths below q_len, empty requests, forced split counts (partials merged by
+the combine kernel), causal q_len > 1, odd head counts, and the full-size
+uniform workload (16 x 4096 keys, 128 heads) on sampled requests in the
+launch configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mla_decode_attention_paged_amd import mla_decode_paged_bf16
+from mla_decode_attention_paged_amd.synth import make_workload, uniform_bf16
+from tests.gpu_helpers import check_gate, extract_requests, say
+from tests.oracle_inputs import oracle_decode_unquantized
+
+pytestmark = pytest.mark.gpu
+
+
+def run_bf16(w, num_splits=None):
+    out = mla_decode_paged_bf16(w.q, w.blocks, w.lookup_table, w.cache_lengths, w.layer_idx, w.q_len,
+                                w.softmax_scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out
+
+
+def _w(gpu_device, *args, **kw):
+    kw.setdefault("device", gpu_device)
+    kw["kv_dtype"] = "bf16"
+    return make_workload(*args, **kw)
+
+
+def test_tiny_poisoned(gpu_device):
+    say("bf16 tiny (B=2, H=16, L={37,100}, P=16, NaN poison)")
+    w = _w(gpu_device, 2, 16, [37, 100], 16, 576, spare_blocks=6, seed=1, poison=True,
+           unused_table_id=0xFFFFFFFF)
+    check_gate(run_bf16(w), oracle_decode_unquantized(w), "bf16 tiny")
+
+
+@pytest.mark.parametrize("splits", [None, 1, 3])
+def test_ragged_tails(gpu_device, splits):
+    lengths = [1, 15, 16, 17, 31, 32, 33, 100, 129, 1000]
+    say("bf16 ragged tails, splits", splits)
+    w = _w(gpu_device, len(lengths), 128, lengths, 64, 576, spare_blocks=2, seed=7, poison=True)
+    check_gate(run_bf16(w, num_splits=splits), oracle_decode_unquantized(w), f"bf16 ragged s{splits}")
+
+
+@pytest.mark.parametrize("q_len,heads,page", [(4, 128, 64), (4, 16, 16), (16, 128, 128), (3, 24, 32)])
+def test_causal_queries(gpu_device, q_len, heads, page):
+    say("bf16 causal", q_len, heads, page)
+    lengths = [q_len, q_len + 5, 300, 2100]
+    w = _w(gpu_device, len(lengths), heads, lengths, page, 576, q_len=q_len, num_layers=3, layer_idx=1,
+           kv_dim=2, spare_blocks=3, seed=11 + q_len + heads, poison=True)
+    check_gate(run_bf16(w), oracle_decode_unquantized(w), f"bf16 causal q{q_len} h{heads} p{page}")
+
+
+def test_empty_and_short_requests(gpu_device):
+    """cache_lengths 0 yields zeros; lengths below q_len leave the first rows empty."""
+    say("bf16 empty / short")
+    w = _w(gpu_device, 4, 16, [5, 2, 40, 9], 16, 576, q_len=4, spare_blocks=1, seed=3, poison=True)
+    w.cache_lengths[0] = 0
+    out = run_bf16(w)
+    assert torch.count_nonzero(out[0]).item() == 0
+    ref = oracle_decode_unquantized(w.to("cpu"))
+    assert (ref[0] == 0).all() and (ref[1, :2] == 0).all()     # request 1: rows 0, 1 see no key
+    assert np.isfinite(out.float().cpu().numpy()).all()
+    check_gate(out[1:], ref[1:], "bf16 short")
+
+
+def test_uniform_full_size_sampled(gpu_device):
+    """16 x 4096 keys, 128 heads, page 64, in the automatic plan (the benchmark's
+    launch configuration); requests 0, 7 and 15 against the oracle."""
+    say("bf16 uniform full size")
+    w = uniform_bf16(device=gpu_device)
+    out = run_bf16(w)
+    batches = [0, 7, 15]
+    sub = extract_requests(w, batches).to("cpu")
+    ref = oracle_decode_unquantized(sub)
+    check_gate(out[batches], ref, "bf16 uniform sampled")
+    assert np.isfinite(out.float().cpu().numpy()).all()
+
+
+def test_long_context_sampled(gpu_device):
+    """One request of 131072 keys (page 128): many splits merged by the combine kernel."""
+    say("bf16 long 131072")
+    w = _w(gpu_device, 1, 128, [131072], 128, 576, seed=3001, poison=False)
+    check_gate(run_bf16(w), oracle_decode_unquantized(w.to("cpu")), "bf16 long")
