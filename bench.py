@@ -32,6 +32,7 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 MALL_BYTES = 256 << 20
 WORKLOADS = ("uniform", "ragged", "long1", "long4", "spec", "chunk", "tiny")
 KERNEL_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "mla_decode.hip")
+KERNEL_SRC_BF16 = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "mla_decode_bf16.hip")
 
 # HBM traffic of one main-kernel launch, from two rocprofv3 --pmc runs of
 # `bench.py --steps 5 --warmup 2 --no-cpu-baseline` (FETCH_SIZE, then
@@ -49,6 +50,10 @@ MEASURED_TRAFFIC = {
     "ef315dbc6813c2e77ba3ef4f9d64ff1ab96bafe38211a20c724c525dcb647706": {
         "uniform_b16_l4096": {"fetch_kib": 19941.30, "write_kib": 32832.0},
     },
+    # unquantized (bf16) cache kernel, `bench.py --op bf16 --steps 5 --warmup 2 --no-cpu-baseline`
+    "9b9d818a8134a858ee70bec2a453ebb376e2f6f3a4a78faa569fd1042dc7cd38": {
+        "uniform_bf16_b16_l4096": {"fetch_kib": 38112.29, "write_kib": 32832.0},
+    },
 }
 
 
@@ -56,8 +61,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def make(name, device):
+def make(name, device, unquantized=False):
     from mla_decode_attention_paged_amd import synth
+    if unquantized:
+        # the same shapes over an unquantized (bf16) cache
+        if name == "uniform":
+            return synth.uniform_bf16(device=device)
+        if name in ("long1", "long4"):
+            B = 1 if name == "long1" else 4
+            return synth.make_workload(B, 128, [131072] * B, 128, 576, seed=3000, device=device, poison=False,
+                                       kv_dtype="bf16", name=f"long_bf16_b{B}")
+        if name == "tiny":
+            return synth.make_workload(2, 16, [37, 100], 16, 576, spare_blocks=6, seed=0, device=device,
+                                       poison=False, kv_dtype="bf16", name="tiny_bf16")
+        raise ValueError(f"workload {name} has no unquantized form here")
     if name == "uniform":
         return synth.uniform(device=device)
     if name == "ragged":
@@ -79,14 +96,18 @@ def replicate_layers(w, min_bytes):
     """Give the cache enough layers that consecutive steps never share a cached layer."""
     import torch
     NB, KVD, NL, P, HK, D = w.blocks.shape
-    layer_bytes = NB * P * D + w.scales.shape[0] * P * w.scales.shape[-1] * 4
+    layer_bytes = NB * P * D * w.blocks.element_size()
+    if w.scales is not None:
+        layer_bytes += w.scales.shape[0] * P * w.scales.shape[-1] * 4
     n = max(NL, int(math.ceil(min_bytes / layer_bytes)))
     if n == NL:
         return w, list(range(NL)) if NL > 1 else [w.layer_idx]
     src_b = w.blocks[:, :, w.layer_idx:w.layer_idx + 1]
-    src_s = w.scales[:, :, w.layer_idx:w.layer_idx + 1]
     blocks = src_b.expand(NB, KVD, n, P, HK, D).contiguous()
-    scales = src_s.expand(w.scales.shape[0], KVD, n, P, HK, w.scales.shape[-1]).contiguous()
+    scales = None
+    if w.scales is not None:
+        src_s = w.scales[:, :, w.layer_idx:w.layer_idx + 1]
+        scales = src_s.expand(w.scales.shape[0], KVD, n, P, HK, w.scales.shape[-1]).contiguous()
     torch.cuda.synchronize()
     w2 = type(w)(**{**w.__dict__, "blocks": blocks, "scales": scales, "layer_idx": 0})
     return w2, list(range(n))
@@ -96,10 +117,12 @@ def algorithmic(w):
     """Algorithmic bytes and flops of one decode call on workload w."""
     lens = w.lengths()
     B, Q, H, D = w.q.shape
-    NG = w.scales.shape[-1]
     P = w.page_size
     tables = 1 if w.scales_lookup_table is None else 2
-    kv_bytes = sum(lens) * (D + 4 * NG)
+    if w.scales is None:                      # unquantized: bf16 rows, no scales
+        kv_bytes = sum(lens) * D * 2
+    else:
+        kv_bytes = sum(lens) * (D + 4 * w.scales.shape[-1])
     table_bytes = sum((L + P - 1) // P for L in lens) * 4 * tables
     io_bytes = B * Q * H * D * 2 + B * Q * H * 512 * 2 + 4 * B
     visible = sum(max(0, min(L, L - Q + i + 1)) for L in lens for i in range(Q))
@@ -134,20 +157,25 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def kernel_digest():
+def kernel_digest(unquantized=False):
     """SHA-256 of the device code in the kernel source (everything between the
     first device helper and the host launchers)."""
     import hashlib
-    with open(KERNEL_SRC, "r") as f:
+    path = KERNEL_SRC_BF16 if unquantized else KERNEL_SRC
+    with open(path, "r") as f:
         src = f.read()
-    a = src.index("// ---------------------------------------------------------------- page resolution")
-    b = src.index("// ---------------------------------------------------------------- host launchers")
+    if unquantized:
+        a = src.index("namespace bf16_path {")
+        b = src.index("// ---------------------------------------------------------------- host launcher")
+    else:
+        a = src.index("// ---------------------------------------------------------------- page resolution")
+        b = src.index("// ---------------------------------------------------------------- host launchers")
     return hashlib.sha256(src[a:b].encode()).hexdigest()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, unquantized=False):
     """HBM bytes per main-kernel launch (read, written, total), or None."""
-    m = MEASURED_TRAFFIC.get(kernel_digest(), {}).get(workload)
+    m = MEASURED_TRAFFIC.get(kernel_digest(unquantized), {}).get(workload)
     if m is None:
         return None
     rd = m["fetch_kib"] * 1024 / _FETCH_PER_KIB
@@ -171,11 +199,15 @@ def cpu_baseline(w):
     import numpy as np
     from threadpoolctl import threadpool_info
     from tests.oracle_inputs import to_numpy
-    from oracle import decode
+    from oracle import decode, decode_unquantized
     wc = w.to("cpu")
     q, blocks, scales, lt, slt, cl = to_numpy(wc)
     blocks = np.ascontiguousarray(blocks[:, :, w.layer_idx:w.layer_idx + 1])
-    scales = np.ascontiguousarray(scales[:, :, w.layer_idx:w.layer_idx + 1])
+    if scales is None:
+        def decode(q, blocks, scales, lt, slt, cl, layer, q_len, sm, batches):  # noqa: F811
+            return decode_unquantized(q, blocks, lt, cl, layer, q_len, sm, batches=batches)
+    else:
+        scales = np.ascontiguousarray(scales[:, :, w.layer_idx:w.layer_idx + 1])
     # run requests in order, cycling, until about 10 s of CPU work is done
     budget_s = 10.0
     t0 = time.perf_counter()
@@ -249,9 +281,10 @@ def main():
     ap.add_argument("--workload", default="uniform", choices=WORKLOADS)
     ap.add_argument("--splits", type=int, default=None, help="explicit split count (default: library plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="decode", choices=("decode", "append"),
-                    help="decode (default, the headline line) or append: the KV append-and-quantize "
-                         "kernel for the workload's q_len new tokens per request")
+    ap.add_argument("--op", default="decode", choices=("decode", "append", "bf16"),
+                    help="decode (default, the headline line); append: the KV append-and-quantize "
+                         "kernel for the workload's q_len new tokens per request; bf16: decode over "
+                         "an unquantized bf16 cache of the workload's shape")
     ap.add_argument("--event-every", type=int, default=5,
                     help="time the main kernel with HIP events on every k-th timed step (events on "
                          "every launch add several microseconds of launch overhead per step)")
@@ -267,17 +300,20 @@ def main():
         calibrate_copy()
         return
     import torch
-    from mla_decode_attention_paged_amd import mla_decode_paged_fp8, mla_decode_paged_fp8_plan, lib_path
+    from mla_decode_attention_paged_amd import (mla_decode_paged_bf16, mla_decode_paged_fp8,
+                                                mla_decode_paged_fp8_plan, lib_path)
 
     dev = torch.device("cuda:0")
-    log(f"bench: workload {args.workload}, library {lib_path()}")
-    w = make(args.workload, dev)
+    log(f"bench: workload {args.workload}, op {args.op}, library {lib_path()}")
+    unq = args.op == "bf16"
+    w = make(args.workload, dev, unquantized=unq)
     if args.op == "append":
         bench_append(args, w)
         return
     w, layers = replicate_layers(w, 2 * MALL_BYTES)
     alg_bytes, alg_flops, kv_tokens = algorithmic(w)
-    plan = mla_decode_paged_fp8_plan(tuple(w.q.shape), tuple(w.blocks.shape), tuple(w.scales.shape),
+    scales_shape = tuple(w.scales.shape) if w.scales is not None else (1,) + tuple(w.blocks.shape[1:5]) + (1,)
+    plan = mla_decode_paged_fp8_plan(tuple(w.q.shape), tuple(w.blocks.shape), scales_shape,
                                      tuple(w.lookup_table.shape), w.q_len, args.splits or 0)
     log(f"bench: layers {len(layers)}, plan {plan}, kv tokens/step {kv_tokens}")
     out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.bfloat16, device=dev)
@@ -287,9 +323,14 @@ def main():
     ev = HipEvents(len(timed))
 
     def step(i, events=None):
-        mla_decode_paged_fp8(w.q, w.blocks, w.scales, w.lookup_table, w.scales_lookup_table,
-                             w.cache_lengths, layers[i % len(layers)], w.q_len, w.softmax_scale,
-                             out=out, workspace=ws, num_splits=args.splits, main_events=events)
+        if unq:
+            mla_decode_paged_bf16(w.q, w.blocks, w.lookup_table, w.cache_lengths, layers[i % len(layers)],
+                                  w.q_len, w.softmax_scale, out=out, workspace=ws, num_splits=args.splits,
+                                  main_events=events)
+        else:
+            mla_decode_paged_fp8(w.q, w.blocks, w.scales, w.lookup_table, w.scales_lookup_table,
+                                 w.cache_lengths, layers[i % len(layers)], w.q_len, w.softmax_scale,
+                                 out=out, workspace=ws, num_splits=args.splits, main_events=events)
 
     for i in range(args.warmup):
         step(i)
@@ -308,7 +349,14 @@ def main():
     log(f"bench: {ms_per_step * 1e3:.1f} us/step, main kernel {kern_avg_ms * 1e3:.1f} us "
         f"(min {min(kern_ms) * 1e3:.1f}), {tflops:.0f} TFLOP/s, {gbs:.0f} GB/s algorithmic")
 
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name, unq)
+    if unq:
+        # arithmetic intensity below the 16-bit ridge (flop per byte < 312.5): HBM binds
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "traffic": (traffic or {}).get("total_bytes"), "traffic_detail": traffic,
+                "kernel": "mla_decode_bf16_kernel", "kernel_avg_us": kern_avg_ms * 1e3,
+                "kernel_timed_launches": len(timed), "alg_flops_per_launch": alg_flops,
+                "alg_bytes_per_launch": alg_bytes, "alg_TFLOPs": tflops, "mfma_frac": tflops / PEAK_MFMA16_TFLOPS}
     result = {
         "metric": "MLA decode KV tokens/s + achieved GB/s & MFMA util vs roofline, 1 MI355X",
         "value": kv_tokens / (ms_per_step * 1e-3),
@@ -320,10 +368,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3-kv/bf16+f16-mfma/fp32-acc",
-        "data": "synthetic (seeded; N(0,1) x LogNormal(0,0.5) latent rows quantised to E4M3FN)",
+        "dtype": "bf16-kv/bf16-mfma/fp32-acc" if unq else "fp8e4m3-kv/bf16+f16-mfma/fp32-acc",
+        "data": ("synthetic (seeded; N(0,1) x LogNormal(0,0.5) latent rows stored as bf16)" if unq else
+                 "synthetic (seeded; N(0,1) x LogNormal(0,0.5) latent rows quantised to E4M3FN)"),
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "num_heads": w.num_heads,
-                   "page_size": w.page_size, "granularity": w.granularity,
+                   "page_size": w.page_size, "granularity": None if unq else w.granularity,
                    "kv_tokens_per_step": kv_tokens, "layers_rotated": len(layers), "plan": plan},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_MFMA16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_MFMA16_TFLOPS,
@@ -334,6 +383,9 @@ def main():
                      "alg_flops_per_launch": alg_flops, "alg_bytes_per_launch": alg_bytes,
                      "alg_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS},
     }
+    if unq:
+        result["metric"] = "MLA decode over an unquantized bf16 paged cache, KV tokens/s, 1 MI355X"
+        result["roofline"] = roof
     if not args.no_cpu_baseline:
         log("bench: timing the FP64 oracle on the host (bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w)

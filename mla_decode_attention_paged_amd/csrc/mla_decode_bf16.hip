@@ -22,8 +22,10 @@
 //     bf16 tile through ds_read_b64_tr_b16, and P is split into a bf16 high
 //     part and a bf16 remainder (two MFMAs per block), which keeps P to about
 //     16 significant bits; 64 MFMAs.
-// Tiles stream global -> LDS by direct-to-LDS loads into a ring of four 36 KiB
-// buffers, three tiles ahead; one workgroup barrier per tile.
+// K and V^T fragments are read from LDS six MFMAs ahead of use, in an order
+// pinned with sched_group_barrier.  Tiles stream global -> LDS by direct-to-LDS
+// loads into a ring of four 36 KiB buffers, three tiles ahead; one workgroup
+// barrier per tile.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -54,6 +56,8 @@ constexpr int kVBlocks = kVDim / 16;             // 32 output blocks of 16 colum
 // Lazy reference maximum: the reference moves only when a score passes it by
 // more than kLazyLog2 / c2, so unnormalised weights stay below 2^kLazyLog2.
 constexpr float kLazyLog2 = 16.0f;
+constexpr int kKAhead = 6;                       // K fragments in flight (depth chunks)
+constexpr int kVAhead = 6;                       // V^T fragments in flight (column blocks)
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
@@ -99,9 +103,12 @@ __device__ __forceinline__ void tile_dma16(const uint8_t* base, uint32_t voff, u
 // LDS tile layout: two halves of 16 keys; in a half, 18 blocks of 1 KiB, block
 // bk holding depth bytes [64 bk, 64 bk + 64) of the 16 keys; inside a block,
 // 16-byte slot 4 k + (c ^ swz(k / 4)) holds bytes [16 c, 16 c + 16) of key k.
-// swz keeps both the 16-key K reads (ds_read_b128) and the 8-key transpose
-// reads of V on distinct banks.
-__device__ __forceinline__ constexpr int swz(int j) { return ((j & 1) << 1) | ((j >> 1) & 1); }
+// swz (0, 2, 3, 1 for k / 4 = 0..3) is a permutation, which keeps the 16-key K
+// reads (ds_read_b128) on distinct banks, and its bit 1 differs between any
+// two groups of four keys that one half-wave of a V transpose read touches
+// (groups 0 and 1, 2 and 3, 0 and 2, 1 and 3), which keeps those reads on
+// distinct banks too.
+__device__ __forceinline__ constexpr int swz(int j) { return (((j ^ (j >> 1)) & 1) << 1) | ((j >> 1) & 1); }
 
 __global__ void __launch_bounds__(kThreadsU) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_decode_bf16_kernel(DecodeArgs a) {
@@ -225,13 +232,29 @@ mla_decode_bf16_kernel(DecodeArgs a) {
 
     LDS_AS const char* tb = L0 + (j % kBufs) * kTileBytesU;
     // ---- S^T for keys 0..15 (sA) and 16..31 (sB) of the tile
+    // (K fragments are read kKAhead depth chunks ahead of their MFMAs)
     f32x4 sA = {0.0f, 0.0f, 0.0f, 0.0f}, sB = {0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 ka[kKAhead], kb[kKAhead];
+#pragma unroll
+    for (int kc = 0; kc < kKAhead; ++kc) {
+      ka[kc] = *(LDS_AS const bf16x8*)(tb + kread + 1024 * kc);
+      kb[kc] = *(LDS_AS const bf16x8*)(tb + kHalfBytes + kread + 1024 * kc);
+    }
 #pragma unroll
     for (int kc = 0; kc < kDepthChunks; ++kc) {
-      const bf16x8 k0 = *(LDS_AS const bf16x8*)(tb + kread + 1024 * kc);
-      const bf16x8 k1 = *(LDS_AS const bf16x8*)(tb + kHalfBytes + kread + 1024 * kc);
-      sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[kc], sA, 0, 0, 0);
-      sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[kc], sB, 0, 0, 0);
+      sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kc % kKAhead], qf[kc], sA, 0, 0, 0);
+      sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kc % kKAhead], qf[kc], sB, 0, 0, 0);
+      if (kc + kKAhead < kDepthChunks) {
+        ka[kc % kKAhead] = *(LDS_AS const bf16x8*)(tb + kread + 1024 * (kc + kKAhead));
+        kb[kc % kKAhead] = *(LDS_AS const bf16x8*)(tb + kHalfBytes + kread + 1024 * (kc + kKAhead));
+      }
+    }
+    // keep that order (the scheduler would otherwise sink each read next to its MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKAhead, 0);
+#pragma unroll
+    for (int kc = 0; kc < kDepthChunks; ++kc) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (kc + kKAhead < kDepthChunks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     // lane (n, gq): x[r] = score of key 4 gq + r (r < 4) or 16 + 4 gq + r - 4, row n
     const int t0 = t_lo + 32 * j;
@@ -272,15 +295,34 @@ mla_decode_bf16_kernel(DecodeArgs a) {
       ph[r] = h;
       pl[r] = (__bf16)(p[r] - (float)h);
     }
-    // ---- O^T += V^T P^T, 16 columns per block
-#pragma unroll
-    for (int nb = 0; nb < kVBlocks; ++nb) {
+    // ---- O^T += V^T P^T, 16 columns per block (V^T fragments read kVAhead blocks ahead)
+    auto read_v = [&](int nb) __attribute__((always_inline)) {
       const uint32_t off = 1024 * (nb >> 1) + vread[nb & 1];
       const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(tb + off));
       const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(tb + kHalfBytes + off));
-      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, o[nb], 0, 0, 0);
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, o[nb], 0, 0, 0);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 va[kVAhead];
+#pragma unroll
+    for (int nb = 0; nb < kVAhead; ++nb) va[nb] = read_v(nb);
+    // blocks go in pairs so that the two MFMAs on one accumulator are not back to back
+#pragma unroll
+    for (int nb = 0; nb < kVBlocks; nb += 2) {
+      const bf16x8 v0 = va[nb % kVAhead], v1 = va[(nb + 1) % kVAhead];
+      if (nb + kVAhead < kVBlocks) {
+        va[nb % kVAhead] = read_v(nb + kVAhead);
+        va[(nb + 1) % kVAhead] = read_v(nb + 1 + kVAhead);
+      }
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, ph, o[nb], 0, 0, 0);
+      o[nb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, ph, o[nb + 1], 0, 0, 0);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pl, o[nb], 0, 0, 0);
+      o[nb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pl, o[nb + 1], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 1);
+#pragma unroll
+    for (int nb = 0; nb < kVBlocks; nb += 2) {
+      if (nb + kVAhead < kVBlocks) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
     }
   }
 
