@@ -32,6 +32,9 @@
  *     and unmodified until the stream has passed the call.
  *   - Arguments are validated on the host before any HIP call.  On any
  *     error nothing is launched and the outputs are untouched.
+ *   - Decode entry points need q, blocks, out and the workspace 16-byte
+ *     aligned and scales, tables and cache_lengths 4-byte aligned
+ *     (MLA_ERR_UNSUPPORTED otherwise); device allocations are.
  *   - Device-side contract (not checked on the device): every page id read
  *     is < num_blocks (values) or < num_scale_blocks (scales); q_len <=
  *     cache_lengths[b] <= max_pages * page_size.  Table columns at or past

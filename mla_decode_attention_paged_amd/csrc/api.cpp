@@ -85,6 +85,10 @@ mla_status make_plan(const mla_shape* s, int32_t q_len, int32_t want_splits, siz
   return MLA_OK;
 }
 
+// The kernels move q, cache rows, outputs and partials in 16-byte pieces and
+// scales, tables and lengths in 4-byte ones.
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
 // Shape check of an unquantized (bf16) cache: the scale fields do not apply.
 mla_status check_shape_unquantized(const mla_shape* s, int32_t q_len) {
   if (!s) return MLA_ERR_NULL;
@@ -110,6 +114,10 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
   if (layer_idx < 0 || layer_idx >= shape->num_layers) return MLA_ERR_RANGE;
   if (num_splits < 0) return MLA_ERR_RANGE;
   if (!isfinite(softmax_scale) || softmax_scale <= 0.0f) return MLA_ERR_RANGE;
+  if (!aligned(q, 16) || !aligned(blocks, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+      (!unquantized && !aligned(scales, 4)) || !aligned(lookup_table, 4) ||
+      (scales_lookup_table && !aligned(scales_lookup_table, 4)) || !aligned(cache_lengths, 4))
+    return MLA_ERR_UNSUPPORTED;
 
   mla_plan plan;
   if (explicit_splits && num_splits > 0) {

@@ -190,3 +190,27 @@ def test_bf16_ignores_scale_fields():
         assert call(lib, good_shape(**kw)) in (SHAPE, UNSUP)
         assert call_bf16(lib, good_shape(**kw), nulls=(0,)) == NULL
         assert call_bf16(lib, good_shape(**kw), layer=5) == RANGE
+
+
+@pytest.mark.parametrize("idx", [0, 1, 5])
+def test_misaligned_pointers_rejected(lib, idx):
+    """q, blocks and out must be 16-byte aligned (checked before any HIP call)."""
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(6)]
+    fake[idx] = ctypes.c_void_p(0x1000 * (idx + 1) + 8)
+    q, blocks, scales, lt, cl, out = fake
+    st = lib.mla_decode_paged_fp8(q, blocks, scales, lt, None, cl, 0, 1, ctypes.c_float(0.07), out,
+                                  ctypes.byref(good_shape()), None, 0, None)
+    assert st == UNSUP
+    if idx != 2:
+        st = lib.mla_decode_paged_bf16(q, blocks, lt, cl, 0, 1, ctypes.c_float(0.07), out,
+                                       ctypes.byref(good_shape()), None, 0, None)
+        assert st == UNSUP
+
+
+def test_misaligned_table_rejected(lib):
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(6)]
+    q, blocks, scales, lt, cl, out = fake
+    lt = ctypes.c_void_p(0x4002)
+    st = lib.mla_decode_paged_fp8(q, blocks, scales, lt, None, cl, 0, 1, ctypes.c_float(0.07), out,
+                                  ctypes.byref(good_shape()), None, 0, None)
+    assert st == UNSUP
