@@ -90,3 +90,10 @@ def test_long_context_sampled(gpu_device):
     say("bf16 long 131072")
     w = _w(gpu_device, 1, 128, [131072], 128, 576, seed=3001, poison=False)
     check_gate(run_bf16(w), oracle_decode_unquantized(w.to("cpu")), "bf16 long")
+
+
+def test_q4_rows_equal_q1_calls(gpu_device):
+    from tests.test_gpu_parity import _q1_calls_match_q4_rows
+    say("bf16 q4 rows vs q1 calls")
+    w = _w(gpu_device, 3, 128, [40, 700, 2100], 64, 576, q_len=4, spare_blocks=2, seed=77, poison=True)
+    _q1_calls_match_q4_rows(w, run_bf16)
