@@ -116,6 +116,12 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // an earlier one (which would raise peak register pressure past the budget).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// 16-byte store with the non-temporal hint (data written once and read once
+// later by another kernel).
+__device__ __forceinline__ void store_nt(float* dst, f32x4 v) {
+  __builtin_nontemporal_store(v, (f32x4*)dst);
+}
+
 // True in every lane when the predicate holds in any lane (wave-uniform result).
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
@@ -586,6 +592,12 @@ mla_decode_kernel(DecodeArgs a) {
   }
 
   // ================================================================ value waves
+  // With per-token scales the value waves carry the step's critical path
+  // (their reads, the tile loads and the PV MFMAs); a higher issue priority
+  // than the score waves on the same SIMD shortens it.  (Measured: 7 % on
+  // the main kernel with 16 x 4096 keys; with group scales it costs 6 %, so
+  // that variant keeps equal priorities.)
+  if constexpr (NG == 1) __builtin_amdgcn_s_setprio(1);
   const int vq4 = sub;                // value wave owns columns [128 vq4, 128 vq4 + 128) of both groups
   // O holds sum_j 2^(c2 (x_j - mO)) s_j v_j for the row's reference max mO,
   // kept per row in LDS (C-layout rows 8(r/4) + 4g + r%4) and in a register
@@ -884,11 +896,12 @@ mla_decode_kernel(DecodeArgs a) {
     } else {
       const size_t pidx = ((size_t)b * a.row_groups + rg) * a.num_splits + split;
       float* po = a.ws_o + pidx * kRows * kVDim + 128 * vq4;
-      // 4 columns (16 bytes) per lane, 2 rows per pass
+      // 4 columns (16 bytes) per lane, 2 rows per pass; non-temporal stores:
+      // the partials are read once, by the combine
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int rl = 2 * k + g;
-        *(f32x4*)(po + rl * kVDim + 4 * n) = *(LDS_AS const f32x4*)(ep + rl * kEpStride + 4 * n);
+        store_nt(po + rl * kVDim + 4 * n, *(LDS_AS const f32x4*)(ep + rl * kEpStride + 4 * n));
       }
       if (vq4 == 0 && g == 0) {
         // the row's log2-sum-exp: c2 mO + log2(L)
@@ -903,26 +916,41 @@ mla_decode_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------- split combine
 // out = sum_s 2^(lse_s - lse) O_s with lse = log2 sum_s 2^lse_s, per row.
-// One workgroup per (request, row group, 64-column chunk); a thread owns one
-// row and 8 columns.
-constexpr int kCombineChunks = kVDim / 64;       // 8
-constexpr int kCombineThreads = kRows * 8;       // 256
+// A workgroup (4 waves) covers (request, row group, a slice of its rows,
+// 64 columns).  In a wave, lane (r, c) owns row r of 8 and columns
+// [8c, 8c + 8): every load of the wave reads 8 rows x 256 contiguous bytes.
+// With SP split groups (SP = 1, 2 or 4, from the split count) the waves of a
+// workgroup split the splits: wave w merges every SP-th batch of eight splits
+// (group w % SP) for row block w / SP, and the groups' running states meet
+// through LDS.  A long request with many splits thus spreads over several
+// workgroups and short per-lane chains.
+constexpr int kCombineThreads = 256;
 
-__global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(DecodeArgs a) {
-  const int chunk = blockIdx.x % kCombineChunks;
-  const int brg = blockIdx.x / kCombineChunks;
+// Split groups: about two batches of eight splits per wave, at most four groups.
+int combine_split_groups(int num_splits) {
+  int sp = 1;
+  while (sp < 4 && 16 * sp < num_splits) sp *= 2;
+  return sp;
+}
+
+__global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(DecodeArgs a, int sp) {
+  __shared__ float st[4][10][64];                   // [wave][M, W, acc[8]][lane]
+  const int chunk = blockIdx.x & 7;                 // 64-column chunk
+  const int rsub = (blockIdx.x >> 3) % sp;          // row slice (32 / sp rows)
+  const int brg = (blockIdx.x >> 3) / sp;
   const int b = brg / a.row_groups;
   const int rg = brg % a.row_groups;
   const int L = (int)min(((const CONST_AS uint32_t*)a.cache_lengths)[b],
                          (uint32_t)a.max_pages * (uint32_t)a.page_size);
   const int T = a.tokens_per_split;
   const int nsplit_eff = L <= 0 ? 1 : (L + T - 1) / T;
-  if (nsplit_eff <= 1) return;
+  if (nsplit_eff <= 1) return;                      // (the whole workgroup)
   const int rows_total = a.q_len * a.num_heads;
-  const int rl = threadIdx.x >> 3;                          // row within the group
-  const int col0 = chunk * 64 + (threadIdx.x & 7) * 8;      // 8 columns per thread
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sg = wave % sp;                         // split group
+  const int rl = rsub * (32 / sp) + 8 * (wave / sp) + (lane >> 3);   // row within the group
+  const int col0 = chunk * 64 + (lane & 7) * 8;     // 8 columns per lane
   const int row = rg * kRows + rl;
-  if (row >= rows_total) return;
 
   const size_t pbase = ((size_t)b * a.row_groups + rg) * a.num_splits;
   // Online over batches of eight splits: each batch's sixteen O loads and
@@ -932,7 +960,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(DecodeArgs
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  for (int s0 = 0; s0 < nsplit_eff; s0 += 8) {
+  for (int s0 = 8 * sg; s0 < nsplit_eff; s0 += 8 * sp) {
     f32x4 v[8][2];
     float ls[8];
 #pragma unroll
@@ -968,6 +996,29 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(DecodeArgs
       }
     }
   }
+  if (sp > 1) {
+    // split groups 1.. hand their states to group 0 of the same row block
+    if (sg != 0) {
+      st[wave][0][lane] = M;
+      st[wave][1][lane] = W;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st[wave][2 + j][lane] = acc[j];
+    }
+    __syncthreads();
+    if (sg != 0) return;
+    for (int k = 1; k < sp; ++k) {
+      const int wo = wave + k;
+      const float Mo = st[wo][0][lane], Wo = st[wo][1][lane];
+      const float Mn = fmaxf(M, Mo);
+      const float r0 = M == kNegInf ? 0.0f : exp2_fast(M - Mn);
+      const float r1 = Mo == kNegInf ? 0.0f : exp2_fast(Mo - Mn);
+      W = W * r0 + Wo * r1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = acc[j] * r0 + st[wo][2 + j][lane] * r1;
+      M = Mn;
+    }
+  }
+  if (row >= rows_total) return;
   const float inv = W > 0.0f ? 1.0f / W : 0.0f;
   uint16_t* orow = a.out + ((size_t)b * rows_total + row) * kVDim + col0;
   u32x4 packed;
@@ -1039,8 +1090,9 @@ hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stre
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(a.batch * a.row_groups * kCombineChunks), dim3(kCombineThreads),
-                     0, stream, a);
+  const int sp = combine_split_groups(a.num_splits);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(a.batch * a.row_groups * 8 * sp), dim3(kCombineThreads), 0, stream,
+                     a, sp);
   return hipGetLastError();
 }
 

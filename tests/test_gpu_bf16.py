@@ -97,3 +97,18 @@ def test_q4_rows_equal_q1_calls(gpu_device):
     say("bf16 q4 rows vs q1 calls")
     w = _w(gpu_device, 3, 128, [40, 700, 2100], 64, 576, q_len=4, spare_blocks=2, seed=77, poison=True)
     _q1_calls_match_q4_rows(w, run_bf16)
+
+
+def test_split_partials_beyond_f16_range(gpu_device):
+    """Cache rows x 2^14 and q x 2^-14: the same scores, O x 2^14, past f16's
+    range; the f16 split partials carry a power-of-two factor per row."""
+    say("bf16 cache, partials beyond the f16 range")
+    w = _w(gpu_device, 2, 128, [3000, 700], 64, 576, seed=74, poison=True, kv_dtype="bf16")
+    w.blocks.mul_(2.0 ** 14)
+    w.q.mul_(2.0 ** -14)
+    ref = oracle_decode_unquantized(w)
+    assert np.abs(ref).max() > 65504.0
+    # the gate is read at the unscaled magnitudes (division by 2^14 is exact)
+    for splits in (1, 2, 7):
+        out = run_bf16(w, num_splits=splits).to(torch.float64) * 2.0 ** -14
+        check_gate(out, ref * 2.0 ** -14, f"bf16 x2^14 splits {splits}")

@@ -204,3 +204,30 @@ def test_q4_rows_equal_q1_calls(gpu_device, gran):
     w = _w(gpu_device, 3, 128, [40, 700, 2100], 64, gran, q_len=4, independent_scales=gran == 64,
            spare_blocks=2, spare_scale_blocks=2, seed=71 + gran, poison=True)
     _q1_calls_match_q4_rows(w, run_gpu)
+
+
+def test_split_partials_beyond_f16_range(gpu_device):
+    """Split partials are stored in f16 with a power-of-two factor per row
+    quarter: outputs far past f16's largest finite value (65504) must still
+    merge correctly.  Scales x 2^14 and q x 2^-14 leave every score unchanged
+    and multiply O by 2^14 exactly (powers of two)."""
+    say("partials beyond the f16 range")
+    w = _w(gpu_device, 2, 128, [3000, 700], 64, 576, seed=73, poison=True)
+    w.scales.mul_(2.0 ** 14)
+    w.q.mul_(2.0 ** -14)
+    ref = oracle_decode(w)
+    assert np.abs(ref).max() > 65504.0
+    # the gate is read at the unscaled magnitudes (division by 2^14 is exact)
+    for splits in (1, 2, 7):
+        out = run_gpu(w, num_splits=splits).to(torch.float64) * 2.0 ** -14
+        check_gate(out, ref * 2.0 ** -14, f"x2^14 splits {splits}")
+
+
+@pytest.mark.parametrize("splits", [40, 157])
+def test_many_splits_ragged(gpu_device, splits):
+    """Many key splits (the combine then merges in several lane groups per row)
+    with requests that use fewer splits than the plan, or none."""
+    say("many splits", splits)
+    w = _w(gpu_device, 3, 128, [20000, 3000, 5], 128, 576, seed=75, poison=True)
+    ref = oracle_decode(w)
+    check_gate(run_gpu(w, num_splits=splits), ref, f"splits {splits}")
