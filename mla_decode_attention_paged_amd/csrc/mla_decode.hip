@@ -245,12 +245,45 @@ mla_decode_kernel(DecodeArgs a) {
   const int g = lane >> 5;          // lane half
   const int n = lane & 31;          // MFMA column / row within the half
 
-  // ---- XCD-aware unit mapping: consecutive units (the row-group pairs of one
-  // key range, which read the same keys) land on the same XCD back to back.
+  // ---- Unit mapping.  A unit is (request, row-group pair, key split),
+  // numbered request-major.  Workgroups are dispatched in blockIdx order and
+  // dealt round-robin to the 8 XCDs (blockIdx % 8); the units of one request
+  // (which read the same keys) are kept on one XCD, back to back.
   const int rgp_count = (a.row_groups + 1) >> 1;
-  const int per_xcd = (a.grid_units + 7) >> 3;
-  const int unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (unit >= a.grid_units) return;
+  int unit;
+  if (a.lpt) {
+    // More units than compute units: longest requests first (a greedy list
+    // schedule in decreasing length keeps the last wave of workgroups
+    // short).  Every workgroup ranks the requests by cache length (ties by
+    // index) in LDS; request rank q goes to XCD q % 8, the ranks of an XCD
+    // in increasing order.
+    LDS_AS uint32_t* const lens = (LDS_AS uint32_t*)L0;
+    LDS_AS uint32_t* const ord = lens + kLptMaxBatch;
+    const uint32_t cap = (uint32_t)a.max_pages * (uint32_t)a.page_size;
+    for (int i = tid; i < a.batch; i += kThreads) lens[i] = min(a.cache_lengths[i], cap);
+    __syncthreads();
+    for (int i = tid; i < a.batch; i += kThreads) {
+      const uint32_t li = lens[i];
+      int rank = 0;
+      for (int j = 0; j < a.batch; ++j) {
+        const uint32_t lj = lens[j];
+        rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
+      }
+      ord[rank] = (uint32_t)i;
+    }
+    __syncthreads();
+    const int ps = rgp_count * a.num_splits;          // units per request
+    const int jx = blockIdx.x >> 3;
+    const int q = (jx / ps) * 8 + (blockIdx.x & 7);   // request rank
+    const int bq = q < a.batch ? (int)ord[q] : 0;
+    __syncthreads();                                  // (the LDS is reused below)
+    if (q >= a.batch) return;
+    unit = bq * ps + jx % ps;
+  } else {
+    const int per_xcd = (a.grid_units + 7) >> 3;
+    unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (unit >= a.grid_units) return;
+  }
   const int rgp = unit % rgp_count;
   const int bs = unit / rgp_count;
   const int split = bs % a.num_splits;
@@ -1066,12 +1099,14 @@ static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream, hipEvent_
     attr_set = true;
   }
   const int per_xcd = (a.grid_units + 7) / 8;
+  // (longest-first order: 8 * ceil(batch / 8) request ranks x units per request)
+  const int grid = a.lpt ? 8 * ((a.batch + 7) / 8) * ((a.row_groups + 1) / 2) * a.num_splits : 8 * per_xcd;
   if (begin && end) {
     // the events take the kernel's own start / end timestamps
-    hipExtLaunchKernelGGL(mla_decode_kernel<NG>, dim3(8 * per_xcd), dim3(kThreads), lds_bytes, stream,
+    hipExtLaunchKernelGGL(mla_decode_kernel<NG>, dim3(grid), dim3(kThreads), lds_bytes, stream,
                           begin, end, 0, a);
   } else {
-    hipLaunchKernelGGL(mla_decode_kernel<NG>, dim3(8 * per_xcd), dim3(kThreads), lds_bytes, stream, a);
+    hipLaunchKernelGGL(mla_decode_kernel<NG>, dim3(grid), dim3(kThreads), lds_bytes, stream, a);
   }
   return hipGetLastError();
 }

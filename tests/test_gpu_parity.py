@@ -231,3 +231,16 @@ def test_many_splits_ragged(gpu_device, splits):
     w = _w(gpu_device, 3, 128, [20000, 3000, 5], 128, 576, seed=75, poison=True)
     ref = oracle_decode(w)
     check_gate(run_gpu(w, num_splits=splits), ref, f"splits {splits}")
+
+
+def test_longest_first_order(gpu_device):
+    """More workgroups than compute units: requests are ranked by length on the
+    device (ties by index) and dealt to the XCDs longest first; a batch that is
+    not a multiple of 8 leaves empty ranks."""
+    rng = np.random.default_rng(77)
+    lengths = rng.integers(4, 400, size=37).tolist()
+    lengths[5] = lengths[6] = lengths[30] = 257                  # ties
+    say("longest-first order, B=37, q_len 4")
+    w = _w(gpu_device, 37, 128, lengths, 64, 64, q_len=4, independent_scales=True, spare_blocks=2,
+           spare_scale_blocks=2, seed=77, poison=True)
+    check_gate(run_gpu(w), oracle_decode(w), "lpt B=37")
