@@ -65,6 +65,17 @@ mla_status make_plan(const mla_shape* s, int32_t q_len, int32_t want_splits, siz
   } else {
     const int64_t target = device_cu_count();
     splits = units >= target ? 1 : (target + units - 1) / units;
+    // Many requests: their lengths usually differ, and two waves of
+    // workgroups dealt largest-first (the kernel's device-side order) keep
+    // the compute units busier than one wave sized for the longest request,
+    // provided the splits stay long (at least kMinWaveSplitKeys keys, so
+    // that per-workgroup fixed costs stay small).  Equal lengths lose
+    // nothing here only when the batch is large; with few requests one wave
+    // is kept.
+    if (s->batch >= 32 && units < target) {
+      const int64_t s2 = (2 * target + units - 1) / units;
+      if ((max_keys + s2 - 1) / s2 >= mla::kMinWaveSplitKeys && s->batch <= mla::kLptMaxBatch) splits = s2;
+    }
     const int64_t min_splits = (max_keys + mla::kMaxSplitKeys - 1) / mla::kMaxSplitKeys;
     if (splits < min_splits) splits = min_splits;
     if (splits > chunks) splits = chunks;
@@ -160,9 +171,9 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
   a.num_splits = plan.num_splits;
   a.tokens_per_split = plan.tokens_per_split;
   a.grid_units = (int32_t)((size_t)shape->batch * ((plan.row_groups + 1) / 2) * plan.num_splits);
-  // longest requests first when the workgroups come in more than one wave
+  // largest key ranges first when the workgroups come in more than one wave
   a.lpt = (!unquantized && shape->batch > 1 && shape->batch <= mla::kLptMaxBatch &&
-           a.grid_units > device_cu_count()) ? 1 : 0;
+           (int64_t)shape->batch * plan.num_splits < 65536 && a.grid_units > device_cu_count()) ? 1 : 0;
   a.sm_log2 = softmax_scale * 1.4426950408889634f;
 
   hipError_t e = unquantized ? mla::launch_decode_bf16(a, stream, main_begin, main_end)

@@ -18,8 +18,10 @@ constexpr int kSplitQuantum = kTile * kWaves;   // split lengths are multiples o
 // that long requests spread over many workgroups (any split length decodes
 // correctly).
 constexpr int kMaxSplitKeys = 8192;
-// Largest batch whose requests the FP8 kernel orders by length on the device.
+// Largest batch whose key ranges the FP8 kernel orders by size on the device.
 constexpr int kLptMaxBatch = 256;
+// Shortest split the plan accepts when it sizes for two waves of workgroups.
+constexpr int kMinWaveSplitKeys = 2048;
 
 // Everything the main kernel needs, by value.  Offsets are precomputed on the
 // host from the contiguous row-major shapes of the blocks / scales tensors.
@@ -40,7 +42,7 @@ struct DecodeArgs {
   int32_t batch, q_len, num_heads, max_pages, page_size;
   int32_t row_groups, num_splits, tokens_per_split;
   int32_t grid_units;                // batch * row_groups * num_splits
-  int32_t lpt;                       // 1: longest requests first (FP8 kernel; batch <= kLptMaxBatch)
+  int32_t lpt;                       // 1: largest (request, split) key ranges first (FP8 kernel)
   float sm_log2;                     // softmax_scale * log2(e)
 };
 

@@ -244,3 +244,22 @@ def test_longest_first_order(gpu_device):
     w = _w(gpu_device, 37, 128, lengths, 64, 64, q_len=4, independent_scales=True, spare_blocks=2,
            spare_scale_blocks=2, seed=77, poison=True)
     check_gate(run_gpu(w), oracle_decode(w), "lpt B=37")
+
+
+def test_largest_key_ranges_first(gpu_device):
+    """Splits with more workgroups than compute units: (request, split) key
+    ranges are ordered by size on the device -- full splits, then the
+    requests' remainders by size, then empty ranges -- covering requests that
+    are empty, exact multiples of the split length, or ragged."""
+    rng = np.random.default_rng(78)
+    lengths = rng.integers(1, 2000, size=40).tolist()
+    lengths[3] = lengths[17] = 0
+    lengths[8] = 512
+    lengths[9] = 1024
+    lengths[20] = lengths[21] = 700                      # equal remainders
+    say("largest key ranges first, B=40, 4 splits")
+    w = _w(gpu_device, 40, 128, lengths, 64, 576, spare_blocks=2, seed=78, poison=True)
+    out = run_gpu(w, num_splits=4)
+    assert (out[3] == 0).all() and (out[17] == 0).all()
+    keep = [b for b in range(40) if lengths[b] > 0]
+    check_gate(out[keep], oracle_decode(w)[keep], "lpt splits 4")
