@@ -50,6 +50,10 @@ MEASURED_TRAFFIC = {
     "f830f38abec473e8feee0cc2b976e31c1fa2beb0bd84acf5415541873cb42166": {
         "uniform_b16_l4096": {"fetch_kib": 19945.7, "write_kib": 32835.1},
     },
+    # unquantized (bf16) cache kernel, `bench.py --op bf16 --steps 5 --warmup 2 --no-cpu-baseline`
+    "9b9d818a8134a858ee70bec2a453ebb376e2f6f3a4a78faa569fd1042dc7cd38": {
+        "uniform_bf16_b16_l4096": {"fetch_kib": 38112.29, "write_kib": 32832.0},
+    },
 }
 
 

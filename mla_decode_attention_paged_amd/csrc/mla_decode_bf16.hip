@@ -343,7 +343,7 @@ mla_decode_bf16_kernel(DecodeArgs a) {
     const size_t pidx = ((size_t)b * a.row_groups + rg) * a.num_splits + split;
     float* po = a.ws_o + (pidx * kRows + row_in_rg) * kVDim + 4 * gq;
 #pragma unroll
-    for (int nb = 0; nb < kVBlocks; ++nb) __builtin_nontemporal_store(o[nb] * inv, (f32x4*)(po + 16 * nb));
+    for (int nb = 0; nb < kVBlocks; ++nb) *(f32x4*)(po + 16 * nb) = o[nb] * inv;
     if (gq == 0) a.ws_lse[pidx * kRows + row_in_rg] = l_row > 0.0f ? m_ref * c2 + __log2f(l_row) : kNegInf;
   }
 }
