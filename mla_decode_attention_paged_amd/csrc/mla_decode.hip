@@ -35,6 +35,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -993,7 +994,8 @@ mla_decode_kernel(DecodeArgs a) {
 // out = sum_s 2^(lse_s - lse) O_s with lse = log2 sum_s 2^lse_s, per row.
 // A workgroup (4 waves) covers (request, row group, a slice of its rows,
 // 64 columns).  In a wave, lane (r, c) owns row r of 8 and columns
-// [8c, 8c + 8): every load of the wave reads 8 rows x 256 contiguous bytes.
+// [4c, 4c + 4) and [32 + 4c, 36 + 4c): every load of the wave reads 8 rows x
+// 128 contiguous bytes.
 // With SP split groups (SP = 1, 2 or 4, from the split count) the waves of a
 // workgroup split the splits: wave w merges every SP-th batch of eight splits
 // (group w % SP) for row block w / SP, and the groups' running states meet
@@ -1024,7 +1026,9 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(DecodeArgs
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sg = wave % sp;                         // split group
   const int rl = rsub * (32 / sp) + 8 * (wave / sp) + (lane >> 3);   // row within the group
-  const int col0 = chunk * 64 + (lane & 7) * 8;     // 8 columns per lane
+  // 8 columns per lane, in two groups of 4 (columns c, c + 32 of the chunk):
+  // each load of the wave then reads 8 rows x 128 contiguous bytes
+  const int col0 = chunk * 64 + (lane & 7) * 4;
   const int row = rg * kRows + rl;
 
   const size_t pbase = ((size_t)b * a.row_groups + rg) * a.num_splits;
@@ -1044,7 +1048,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(DecodeArgs
       ls[u] = a.ws_lse[(pbase + s) * kRows + rl];
       const f32x4* src = (const f32x4*)(a.ws_o + ((pbase + s) * kRows + rl) * kVDim + col0);
       v[u][0] = src[0];
-      v[u][1] = src[1];
+      v[u][1] = src[8];
     }
     float mb = kNegInf;
 #pragma unroll
@@ -1096,11 +1100,14 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(DecodeArgs
   if (row >= rows_total) return;
   const float inv = W > 0.0f ? 1.0f / W : 0.0f;
   uint16_t* orow = a.out + ((size_t)b * rows_total + row) * kVDim + col0;
-  u32x4 packed;
+  u32x2 lo, hi;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    packed[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
-  *(u32x4*)orow = packed;
+  for (int j = 0; j < 2; ++j) {
+    lo[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
+    hi[j] = (uint32_t)f32_to_bf16_bits(acc[4 + 2 * j] * inv) | ((uint32_t)f32_to_bf16_bits(acc[5 + 2 * j] * inv) << 16);
+  }
+  *(u32x2*)orow = lo;
+  *(u32x2*)(orow + 32) = hi;
 }
 
 // ---------------------------------------------------------------- resolve (debug)
