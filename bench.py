@@ -47,8 +47,8 @@ _COPY_KIB = 1048576.0
 _FETCH_PER_KIB = 524302.5 / _COPY_KIB
 _WRITE_PER_KIB = 1048576.0 / _COPY_KIB
 MEASURED_TRAFFIC = {
-    "f830f38abec473e8feee0cc2b976e31c1fa2beb0bd84acf5415541873cb42166": {
-        "uniform_b16_l4096": {"fetch_kib": 19945.7, "write_kib": 32835.1},
+    "79468cfd6be2f8a666b7f1fbd46c9cde6e8a374123a8be995e160edef3b694d8": {
+        "uniform_b16_l4096": {"fetch_kib": 19945.8, "write_kib": 32833.3},
     },
     # unquantized (bf16) cache kernel, `bench.py --op bf16 --steps 5 --warmup 2 --no-cpu-baseline`
     "9b9d818a8134a858ee70bec2a453ebb376e2f6f3a4a78faa569fd1042dc7cd38": {
