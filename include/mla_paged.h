@@ -99,7 +99,11 @@ typedef struct {
   int32_t row_groups;        /* ceil(q_len * num_q_heads / 32)                     */
   int32_t num_splits;        /* key-range splits per (request, row group)          */
   int32_t tokens_per_split;  /* keys per split, a multiple of 128                  */
-  int32_t grid;              /* workgroups of the main kernel                      */
+  int32_t grid;              /* workgroups of the main kernel in request order; with
+                                more workgroups than compute units (batch <= 256) the
+                                FP8 kernel deals (request, split) key ranges largest
+                                first and may launch up to 8 * ceil(q_len * heads / 64)
+                                more, which exit at once                          */
   size_t workspace_bytes;    /* split partials; 0 when num_splits == 1             */
 } mla_plan;
 

@@ -214,3 +214,18 @@ def test_misaligned_table_rejected(lib):
     st = lib.mla_decode_paged_fp8(q, blocks, scales, lt, None, cl, 0, 1, ctypes.c_float(0.07), out,
                                   ctypes.byref(good_shape()), None, 0, None)
     assert st == UNSUP
+
+
+def test_plan_two_waves_for_large_batches(lib):
+    """With >= 32 requests the automatic plan sizes for two waves of workgroups
+    (the kernel deals key ranges largest first), as long as a split keeps at
+    least 2048 keys; otherwise one wave.  (CPU: the CU count defaults to 256.)"""
+    def splits(B, maxp, P=64, Q=1):
+        st, p = plan(lib, good_shape(batch=B, max_pages=maxp, page_size=P, num_blocks=maxp * B), q_len=Q)
+        assert st == OK
+        return p.num_splits, p.tokens_per_split
+    assert splits(64, 128) == (4, 2048)         # 128 units -> 512 workgroups
+    assert splits(16, 64) == (8, 512)           # few requests: one wave
+    assert splits(4, 1024, P=128) == (32, 4096)
+    assert splits(32, 16) == (4, 256)           # two waves would cut splits below 2048 keys
+    assert splits(300, 16)[0] == 1              # more units than compute units already
