@@ -263,3 +263,23 @@ def test_largest_key_ranges_first(gpu_device):
     assert (out[3] == 0).all() and (out[17] == 0).all()
     keep = [b for b in range(40) if lengths[b] > 0]
     check_gate(out[keep], oracle_decode(w)[keep], "lpt splits 4")
+
+
+@pytest.mark.parametrize("case", [
+    # (batch, heads, q_len, page, granularity, max length, seed): default plans that
+    # put more workgroups than compute units in flight (largest-first order), with
+    # one split, two splits and seven splits per request
+    (200, 128, 1, 16, 576, 200, 81),
+    (48, 128, 2, 64, 64, 3000, 82),
+    (40, 64, 1, 128, 576, 4300, 83),
+])
+def test_default_plans_over_one_wave(gpu_device, case):
+    B, H, Q, P, G, lmax, seed = case
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(Q, lmax + 1, size=B).tolist()
+    lengths[0] = lmax
+    lengths[-1] = Q
+    say("default plan over one wave", case)
+    w = _w(gpu_device, B, H, lengths, P, G, q_len=Q, independent_scales=G == 64, spare_blocks=2,
+           spare_scale_blocks=2, seed=seed, poison=True)
+    check_gate(run_gpu(w), oracle_decode(w), f"plan {case}")
