@@ -223,7 +223,7 @@ def test_split_partials_beyond_f16_range(gpu_device):
         check_gate(out, ref * 2.0 ** -14, f"x2^14 splits {splits}")
 
 
-@pytest.mark.parametrize("splits", [40, 157])
+@pytest.mark.parametrize("splits", [24, 40, 157])
 def test_many_splits_ragged(gpu_device, splits):
     """Many key splits (the combine then merges in several lane groups per row)
     with requests that use fewer splits than the plan, or none."""
