@@ -33,6 +33,7 @@ MALL_BYTES = 256 << 20
 WORKLOADS = ("uniform", "ragged", "long1", "long4", "spec", "chunk", "tiny")
 KERNEL_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "mla_decode.hip")
 KERNEL_SRC_BF16 = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "mla_decode_bf16.hip")
+UNIT_ORDER_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "unit_order.h")
 
 # HBM traffic of one main-kernel launch, from two rocprofv3 --pmc runs of
 # `bench.py --steps 5 --warmup 2 --no-cpu-baseline` (FETCH_SIZE, then
@@ -159,7 +160,8 @@ class HipEvents:
 
 def kernel_digest(unquantized=False):
     """SHA-256 of the device code in the kernel source (everything between the
-    first device helper and the host launchers)."""
+    first device helper and the host launchers) and of the shared unit
+    mapping (unit_order.h)."""
     import hashlib
     path = KERNEL_SRC_BF16 if unquantized else KERNEL_SRC
     with open(path, "r") as f:
@@ -170,7 +172,9 @@ def kernel_digest(unquantized=False):
     else:
         a = src.index("// ---------------------------------------------------------------- page resolution")
         b = src.index("// ---------------------------------------------------------------- host launchers")
-    return hashlib.sha256(src[a:b].encode()).hexdigest()
+    with open(UNIT_ORDER_SRC, "r") as f:       # the workgroup -> unit mapping both kernels use
+        order = f.read()
+    return hashlib.sha256((src[a:b] + order).encode()).hexdigest()
 
 
 def measured_traffic(workload, unquantized=False):

@@ -172,7 +172,7 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
   a.tokens_per_split = plan.tokens_per_split;
   a.grid_units = (int32_t)((size_t)shape->batch * ((plan.row_groups + 1) / 2) * plan.num_splits);
   // largest key ranges first when the workgroups come in more than one wave
-  a.lpt = (!unquantized && shape->batch > 1 && shape->batch <= mla::kLptMaxBatch &&
+  a.lpt = (shape->batch > 1 && shape->batch <= mla::kLptMaxBatch &&
            (int64_t)shape->batch * plan.num_splits < 65536 && a.grid_units > device_cu_count()) ? 1 : 0;
   a.sm_log2 = softmax_scale * 1.4426950408889634f;
 

@@ -27,6 +27,7 @@
 #include <hip/hip_ext.h>
 
 #include "mla_internal.h"
+#include "unit_order.h"
 
 namespace mla {
 
@@ -246,87 +247,11 @@ mla_decode_kernel(DecodeArgs a) {
   const int g = lane >> 5;          // lane half
   const int n = lane & 31;          // MFMA column / row within the half
 
-  // ---- Unit mapping.  A unit is (request, row-group pair, key split),
-  // numbered request-major.  Workgroups are dispatched in blockIdx order and
-  // dealt round-robin to the 8 XCDs (blockIdx % 8); the units of one request
-  // (which read the same keys) are kept on one XCD, back to back.
+  // ---- The work unit (request, row-group pair, key split) of this
+  // workgroup: request order, or largest key ranges first (unit_order.h).
   const int rgp_count = (a.row_groups + 1) >> 1;
-  int unit;
-  if (a.lpt) {
-    // More units than compute units: largest key ranges first (the
-    // hardware's in-order dispatch then runs a greedy list schedule in
-    // decreasing size, which keeps the last wave of workgroups short).  An
-    // item is a (request, split) key range; its key count is T for the full
-    // splits of a request, the remainder for its last split, 0 past it.
-    // Items are ranked by (count desc, index asc): first every full split
-    // in index order, then the requests' remainders by size (ties by
-    // request; a request without keys has a remainder of 0 keys, so that its
-    // zero output is written), then the empty items.  Every workgroup computes the item at
-    // its own rank from the cache lengths: a prefix sum of the full-split
-    // counts and a ranking of the <= kLptMaxBatch remainders, in LDS.  Item
-    // rank q goes to XCD q % 8, the ranks of an XCD in increasing order,
-    // each item's row-group pairs back to back.
-    LDS_AS int* const fpre = (LDS_AS int*)L0;                   // [B + 1] full splits before request b
-    LDS_AS int* const tail = fpre + kLptMaxBatch + 1;           // [B] remainder keys of request b
-    LDS_AS int* const tord = tail + kLptMaxBatch;               // [B] requests by remainder rank
-    LDS_AS int* const wsum = tord + kLptMaxBatch;               // [4] per-wave totals of the scan
-    const int T = a.tokens_per_split, S = a.num_splits, B = a.batch;
-    const uint32_t cap = (uint32_t)a.max_pages * (uint32_t)a.page_size;
-    // full splits (low 16 bits) and remainder flag (high 16 bits) of request tid,
-    // scanned over the first four waves (B <= 256)
-    // A request with no keys still writes its (zero) output: its split 0
-    // counts as a remainder of 0 keys.  tail[b] = -1: no remainder.
-    int fb = 0, tb = -1;
-    if (tid < B) {
-      const int len = (int)min(a.cache_lengths[tid], cap);
-      fb = min(S, len / T);
-      tb = (fb < S && (len > fb * T || len == 0)) ? len - fb * T : -1;
-      tail[tid] = tb;
-    }
-    int v = fb | ((tb >= 0 ? 1 : 0) << 16);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int u = __shfl_up(v, off);
-      if (lane >= off) v += u;
-    }
-    if (lane == 63 && wave < 4) wsum[wave] = v;
-    __syncthreads();
-    for (int w = 0; w < wave && w < 4; ++w) v += wsum[w];
-    if (tid < B) fpre[tid + 1] = v & 0xffff;
-    if (tid == 0) fpre[0] = 0;
-    const int tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];     // (all four waves' totals)
-    const int F = tot & 0xffff, NT = tot >> 16;
-    if (tid < B && tb >= 0) {
-      int rank = 0;
-      for (int j = 0; j < B; ++j) {
-        const int tj = tail[j];
-        rank += (tj > tb || (tj == tb && j < tid)) ? 1 : 0;
-      }
-      tord[rank] = tid;
-    }
-    __syncthreads();
-    const int jx = blockIdx.x >> 3;
-    const int q = (jx / rgp_count) * 8 + (blockIdx.x & 7);     // item rank
-    int item = -1;
-    if (q < F) {
-      int lo = 0, hi = B - 1;          // the request b with fpre[b] <= q < fpre[b + 1]
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (fpre[mid] <= q) lo = mid; else hi = mid - 1;
-      }
-      item = lo * S + (q - fpre[lo]);
-    } else if (q < F + NT) {
-      const int bt = tord[q - F];
-      item = bt * S + (fpre[bt + 1] - fpre[bt]);
-    }
-    __syncthreads();                                  // (the LDS is reused below)
-    if (item < 0) return;                             // an empty key range
-    unit = item * rgp_count + jx % rgp_count;
-    } else {
-    const int per_xcd = (a.grid_units + 7) >> 3;
-    unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if (unit >= a.grid_units) return;
-  }
+  const int unit = workgroup_unit(a, rgp_count, L0, tid, lane, wave);
+  if (unit < 0) return;
   const int rgp = unit % rgp_count;
   const int bs = unit / rgp_count;
   const int split = bs % a.num_splits;
@@ -1147,9 +1072,7 @@ static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream, hipEvent_
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int per_xcd = (a.grid_units + 7) / 8;
-  // (largest-first order: 8 * ceil(items / 8) item ranks x row-group pairs per item)
-  const int grid = a.lpt ? 8 * ((a.batch * a.num_splits + 7) / 8) * ((a.row_groups + 1) / 2) : 8 * per_xcd;
+  const int grid = decode_grid(a);
   if (begin && end) {
     // the events take the kernel's own start / end timestamps
     hipExtLaunchKernelGGL(mla_decode_kernel<NG>, dim3(grid), dim3(kThreads), lds_bytes, stream,

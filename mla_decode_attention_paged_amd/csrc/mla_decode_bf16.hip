@@ -30,6 +30,7 @@
 #include <hip/hip_ext.h>
 
 #include "mla_internal.h"
+#include "unit_order.h"
 
 namespace mla {
 namespace bf16_path {
@@ -121,11 +122,10 @@ mla_decode_bf16_kernel(DecodeArgs a) {
   const int gq = lane >> 4;           // 16-lane group
   const int n = lane & 15;
 
-  // ---- unit: (request, row-group pair, key split), XCD-aware as in the FP8 kernel
+  // ---- unit: (request, row-group pair, key split), in the FP8 kernel's order
   const int rgp_count = (a.row_groups + 1) >> 1;
-  const int per_xcd = (a.grid_units + 7) >> 3;
-  const int unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (unit >= a.grid_units) return;
+  const int unit = workgroup_unit(a, rgp_count, L0, tid, lane, wave);
+  if (unit < 0) return;
   const int rgp = unit % rgp_count;
   const int bs = unit / rgp_count;
   const int split = bs % a.num_splits;
@@ -363,12 +363,12 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, hipEvent_
   hipError_t e;
   const bool both = main_begin && main_end;
   if (main_begin && !both && (e = hipEventRecord(main_begin, stream)) != hipSuccess) return e;
-  const int per_xcd = (a.grid_units + 7) / 8;
+  const int grid = decode_grid(a);
   if (both) {
-    hipExtLaunchKernelGGL(bf16_path::mla_decode_bf16_kernel, dim3(8 * per_xcd), dim3(bf16_path::kThreadsU),
+    hipExtLaunchKernelGGL(bf16_path::mla_decode_bf16_kernel, dim3(grid), dim3(bf16_path::kThreadsU),
                           bf16_path::kLdsBytes, stream, main_begin, main_end, 0, a);
   } else {
-    hipLaunchKernelGGL(bf16_path::mla_decode_bf16_kernel, dim3(8 * per_xcd), dim3(bf16_path::kThreadsU),
+    hipLaunchKernelGGL(bf16_path::mla_decode_bf16_kernel, dim3(grid), dim3(bf16_path::kThreadsU),
                        bf16_path::kLdsBytes, stream, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;

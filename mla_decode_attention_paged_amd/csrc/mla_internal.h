@@ -18,7 +18,7 @@ constexpr int kSplitQuantum = kTile * kWaves;   // split lengths are multiples o
 // that long requests spread over many workgroups (any split length decodes
 // correctly).
 constexpr int kMaxSplitKeys = 8192;
-// Largest batch whose key ranges the FP8 kernel orders by size on the device.
+// Largest batch whose key ranges the decode kernels order by size on the device.
 constexpr int kLptMaxBatch = 256;
 // Shortest split the plan accepts when it sizes for two waves of workgroups.
 constexpr int kMinWaveSplitKeys = 2048;
@@ -42,7 +42,7 @@ struct DecodeArgs {
   int32_t batch, q_len, num_heads, max_pages, page_size;
   int32_t row_groups, num_splits, tokens_per_split;
   int32_t grid_units;                // batch * row_groups * num_splits
-  int32_t lpt;                       // 1: largest (request, split) key ranges first (FP8 kernel)
+  int32_t lpt;                       // 1: largest (request, split) key ranges first
   float sm_log2;                     // softmax_scale * log2(e)
 };
 

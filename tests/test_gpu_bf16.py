@@ -112,3 +112,19 @@ def test_split_partials_beyond_f16_range(gpu_device):
     for splits in (1, 2, 7):
         out = run_bf16(w, num_splits=splits).to(torch.float64) * 2.0 ** -14
         check_gate(out, ref * 2.0 ** -14, f"bf16 x2^14 splits {splits}")
+
+
+def test_largest_key_ranges_first(gpu_device):
+    """More workgroups than compute units over the bf16 cache: key ranges run
+    largest first, with empty requests and exact multiples of the split."""
+    rng = np.random.default_rng(79)
+    lengths = rng.integers(1, 2000, size=40).tolist()
+    lengths[2] = 0
+    lengths[11] = 512
+    lengths[30] = lengths[31] = 900
+    say("bf16 cache, largest key ranges first, B=40, 4 splits")
+    w = _w(gpu_device, 40, 128, lengths, 64, 576, spare_blocks=2, seed=79, poison=True)
+    out = run_bf16(w, num_splits=4)
+    assert (out[2] == 0).all()
+    keep = [b for b in range(40) if lengths[b] > 0]
+    check_gate(out[keep], oracle_decode_unquantized(w)[keep], "bf16 lpt splits 4")
