@@ -48,12 +48,12 @@ _COPY_KIB = 1048576.0
 _FETCH_PER_KIB = 524302.5 / _COPY_KIB
 _WRITE_PER_KIB = 1048576.0 / _COPY_KIB
 MEASURED_TRAFFIC = {
-    "79468cfd6be2f8a666b7f1fbd46c9cde6e8a374123a8be995e160edef3b694d8": {
-        "uniform_b16_l4096": {"fetch_kib": 19945.8, "write_kib": 32833.3},
+    "6ba91bb1113d5bdd519cfba6523a6d79bd6a8d2ace83039b7a639be8e89119cb": {
+        "uniform_b16_l4096": {"fetch_kib": 19945.8, "write_kib": 32834.5},
     },
     # unquantized (bf16) cache kernel, `bench.py --op bf16 --steps 5 --warmup 2 --no-cpu-baseline`
-    "9b9d818a8134a858ee70bec2a453ebb376e2f6f3a4a78faa569fd1042dc7cd38": {
-        "uniform_bf16_b16_l4096": {"fetch_kib": 38112.29, "write_kib": 32832.0},
+    "c922b2d7e1f194d3cc7007ddec384574229a40d4fecac90a71d869bf2a7cf6ec": {
+        "uniform_bf16_b16_l4096": {"fetch_kib": 38123.3, "write_kib": 32832.0},
     },
 }
 
