@@ -66,12 +66,12 @@ mla_status make_plan(const mla_shape* s, int32_t q_len, int32_t want_splits, siz
     const int64_t target = device_cu_count();
     splits = units >= target ? 1 : (target + units - 1) / units;
     // Many requests: their lengths usually differ, and two waves of
-    // workgroups dealt largest-first (the kernel's device-side order) keep
+    // workgroups dealt largest-first (the kernels' device-side order) keep
     // the compute units busier than one wave sized for the longest request,
     // provided the splits stay long (at least kMinWaveSplitKeys keys, so
-    // that per-workgroup fixed costs stay small).  Equal lengths lose
-    // nothing here only when the batch is large; with few requests one wave
-    // is kept.
+    // that per-workgroup fixed costs stay small).  With equal lengths the
+    // second wave only adds those fixed costs, hence the rule is kept to
+    // batches of 32 requests or more; smaller batches keep one wave.
     if (s->batch >= 32 && units < target) {
       const int64_t s2 = (2 * target + units - 1) / units;
       if ((max_keys + s2 - 1) / s2 >= mla::kMinWaveSplitKeys && s->batch <= mla::kLptMaxBatch) splits = s2;
