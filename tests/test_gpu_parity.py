@@ -268,10 +268,11 @@ def test_largest_key_ranges_first(gpu_device):
 @pytest.mark.parametrize("case", [
     # (batch, heads, q_len, page, granularity, max length, seed): default plans that
     # put more workgroups than compute units in flight (largest-first order), with
-    # one split, two splits and seven splits per request
+    # one, two and seven splits per request
     (200, 128, 1, 16, 576, 200, 81),
     (48, 128, 2, 64, 64, 3000, 82),
     (40, 64, 1, 128, 576, 4300, 83),
+    (200, 16, 1, 16, 576, 300, 84),           # one row group: the pair's second group is absent
 ])
 def test_default_plans_over_one_wave(gpu_device, case):
     B, H, Q, P, G, lmax, seed = case
