@@ -153,6 +153,13 @@ class HipEvents:
         assert self.hip.hipEventElapsedTime(ctypes.byref(ms), *[ctypes.c_void_p(x) for x in self.pair(i)]) == 0
         return ms.value
 
+    def elapsed_to_torch_event_ms(self, i, tev):
+        """From the end event of pair i to a later torch.cuda.Event on the same stream."""
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.pair(i)[1]),
+                                            ctypes.c_void_p(tev.cuda_event)) == 0
+        return ms.value
+
     def close(self):
         for e in self.ev:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
@@ -225,11 +232,16 @@ def cpu_baseline(w):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    pools = threadpool_info()
+    blas = [i for i in pools if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
     return {"value": done_tokens / dt, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas": ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                              for i in blas) or "none",
             "sample": f"{calls} single-request oracle calls cycling over the {B} requests of one layer of the "
                       f"same workload ({done_tokens} cached tokens, all {w.num_heads} heads, q_len {w.q_len}), "
-                      f"{dt:.1f} s wall"}
+                      f"{dt:.1f} s wall; cores = the BLAS threads the oracle's matrix products used"}
 
 
 def bench_append(args, w):
@@ -285,6 +297,9 @@ def main():
     ap.add_argument("--workload", default="uniform", choices=WORKLOADS)
     ap.add_argument("--splits", type=int, default=None, help="explicit split count (default: library plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the selected workload (by default the uniform headline line also carries "
+                         "the ragged, long-context and speculative workloads in its 'configs' object)")
     ap.add_argument("--op", default="decode", choices=("decode", "append", "bf16"),
                     help="decode (default, the headline line); append: the KV append-and-quantize "
                          "kernel for the workload's q_len new tokens per request; bf16: decode over "
@@ -304,8 +319,7 @@ def main():
         calibrate_copy()
         return
     import torch
-    from mla_decode_attention_paged_amd import (mla_decode_paged_bf16, mla_decode_paged_fp8,
-                                                mla_decode_paged_fp8_plan, lib_path)
+    from mla_decode_attention_paged_amd import lib_path
 
     dev = torch.device("cuda:0")
     log(f"bench: workload {args.workload}, op {args.op}, library {lib_path()}")
@@ -314,61 +328,15 @@ def main():
     if args.op == "append":
         bench_append(args, w)
         return
-    w, layers = replicate_layers(w, 2 * MALL_BYTES)
-    alg_bytes, alg_flops, kv_tokens = algorithmic(w)
-    scales_shape = tuple(w.scales.shape) if w.scales is not None else (1,) + tuple(w.blocks.shape[1:5]) + (1,)
-    plan = mla_decode_paged_fp8_plan(tuple(w.q.shape), tuple(w.blocks.shape), scales_shape,
-                                     tuple(w.lookup_table.shape), w.q_len, args.splits or 0)
-    log(f"bench: layers {len(layers)}, plan {plan}, kv tokens/step {kv_tokens}")
-    out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
-    every = max(1, args.event_every)
-    timed = [i for i in range(args.steps) if i % every == 0]
-    ev = HipEvents(len(timed))
-
-    def step(i, events=None):
-        if unq:
-            mla_decode_paged_bf16(w.q, w.blocks, w.lookup_table, w.cache_lengths, layers[i % len(layers)],
-                                  w.q_len, w.softmax_scale, out=out, workspace=ws, num_splits=args.splits,
-                                  main_events=events)
-        else:
-            mla_decode_paged_fp8(w.q, w.blocks, w.scales, w.lookup_table, w.scales_lookup_table,
-                                 w.cache_lengths, layers[i % len(layers)], w.q_len, w.softmax_scale,
-                                 out=out, workspace=ws, num_splits=args.splits, main_events=events)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, ev.pair(i // every) if i % every == 0 else None)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = [ev.elapsed_ms(k) for k in range(len(timed))]
-    ev.close()
-    kern_avg_ms = sum(kern_ms) / len(kern_ms)
-    tflops = alg_flops / (kern_avg_ms * 1e-3) / 1e12
-    gbs = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
-    log(f"bench: {ms_per_step * 1e3:.1f} us/step, main kernel {kern_avg_ms * 1e3:.1f} us "
-        f"(min {min(kern_ms) * 1e3:.1f}), {tflops:.0f} TFLOP/s, {gbs:.0f} GB/s algorithmic")
-
-    traffic = measured_traffic(w.name, unq)
-    if unq:
-        # arithmetic intensity below the 16-bit ridge (flop per byte < 312.5): HBM binds
-        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                "traffic": (traffic or {}).get("total_bytes"), "traffic_detail": traffic,
-                "kernel": "mla_decode_bf16_kernel", "kernel_avg_us": kern_avg_ms * 1e3,
-                "kernel_timed_launches": len(timed), "alg_flops_per_launch": alg_flops,
-                "alg_bytes_per_launch": alg_bytes, "alg_TFLOPs": tflops, "mfma_frac": tflops / PEAK_MFMA16_TFLOPS}
+    r = time_decode(w, args.steps, args.warmup, args.splits, args.event_every, unq)
     result = {
         "metric": "MLA decode KV tokens/s + achieved GB/s & MFMA util vs roofline, 1 MI355X",
-        "value": kv_tokens / (ms_per_step * 1e-3),
+        "value": r["kv_tokens"] / (r["ms_per_step"] * 1e-3),
         "unit": "KV tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -377,23 +345,110 @@ def main():
                  "synthetic (seeded; N(0,1) x LogNormal(0,0.5) latent rows quantised to E4M3FN)"),
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "num_heads": w.num_heads,
                    "page_size": w.page_size, "granularity": None if unq else w.granularity,
-                   "kv_tokens_per_step": kv_tokens, "layers_rotated": len(layers), "plan": plan},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_MFMA16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_MFMA16_TFLOPS,
-                     "traffic": (traffic or {}).get("total_bytes"),
-                     "traffic_detail": traffic,
-                     "kernel": "mla_decode_kernel", "kernel_avg_us": kern_avg_ms * 1e3,
-                     "kernel_timed_launches": len(timed),
-                     "alg_flops_per_launch": alg_flops, "alg_bytes_per_launch": alg_bytes,
-                     "alg_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS},
+                   "kv_tokens_per_step": r["kv_tokens"], "layers_rotated": r["layers"], "plan": r["plan"]},
+        "roofline": r["roofline"],
     }
     if unq:
         result["metric"] = "MLA decode over an unquantized bf16 paged cache, KV tokens/s, 1 MI355X"
-        result["roofline"] = roof
+    if not args.no_configs and not unq and args.workload == "uniform" and args.splits is None:
+        # the other workloads of the same path, each timed the same way (fewer steps)
+        configs = {}
+        for name in ("ragged", "long1", "long4", "spec"):
+            wc = make(name, dev)
+            steps, warm = (10, 3) if name == "spec" else (20, 5)
+            rc = time_decode(wc, steps, warm, None, 5, False)
+            rf = rc["roofline"]
+            configs[wc.name] = {
+                "kv_tokens_per_s": rc["kv_tokens"] / (rc["ms_per_step"] * 1e-3), "steps": steps,
+                "step_us": rc["ms_per_step"] * 1e3, "main_kernel_us": rf["kernel_avg_us"],
+                "after_main_us": rc["after_main_us"], "frac": rf["frac"], "step_frac": rf["step_frac"],
+                "bound": rf["bound"], "alg_flops": rf["alg_flops_per_launch"], "alg_bytes": rf["alg_bytes_per_launch"],
+                "traffic": rf["traffic"], "plan": rc["plan"]}
+            del wc
+            torch.cuda.empty_cache()
+        result["configs"] = configs
     if not args.no_cpu_baseline:
         log("bench: timing the FP64 oracle on the host (bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)
+
+
+def time_decode(w, steps, warmup, splits, event_every, unq):
+    """Time `steps` decode calls on workload w (after `warmup` untimed ones);
+    returns the step rate, the main kernel's own time and the roofline record."""
+    import torch
+    from mla_decode_attention_paged_amd import (mla_decode_paged_bf16, mla_decode_paged_fp8,
+                                                mla_decode_paged_fp8_plan)
+    dev = w.q.device
+    w, layers = replicate_layers(w, 2 * MALL_BYTES)
+    alg_bytes, alg_flops, kv_tokens = algorithmic(w)
+    scales_shape = tuple(w.scales.shape) if w.scales is not None else (1,) + tuple(w.blocks.shape[1:5]) + (1,)
+    plan = mla_decode_paged_fp8_plan(tuple(w.q.shape), tuple(w.blocks.shape), scales_shape,
+                                     tuple(w.lookup_table.shape), w.q_len, splits or 0)
+    log(f"bench: {w.name}: layers {len(layers)}, plan {plan}, kv tokens/step {kv_tokens}")
+    out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+    every = max(1, event_every)
+    timed = [i for i in range(steps) if i % every == 0]
+    ev = HipEvents(len(timed))
+    after = [torch.cuda.Event(enable_timing=True) for _ in timed]
+
+    def step(i, events=None):
+        if unq:
+            mla_decode_paged_bf16(w.q, w.blocks, w.lookup_table, w.cache_lengths, layers[i % len(layers)],
+                                  w.q_len, w.softmax_scale, out=out, workspace=ws, num_splits=splits,
+                                  main_events=events)
+        else:
+            mla_decode_paged_fp8(w.q, w.blocks, w.scales, w.lookup_table, w.scales_lookup_table,
+                                 w.cache_lengths, layers[i % len(layers)], w.q_len, w.softmax_scale,
+                                 out=out, workspace=ws, num_splits=splits, main_events=events)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if i % every == 0:
+            step(warmup + i, ev.pair(i // every))
+            after[i // every].record()
+        else:
+            step(warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    kern_ms = [ev.elapsed_ms(k) for k in range(len(timed))]
+    # main kernel end -> the call's last work on the stream (split combine and launch gap)
+    after_ms = [ev.elapsed_to_torch_event_ms(k, after[k]) for k in range(len(timed))]
+    ev.close()
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    tflops = alg_flops / (kern_avg_ms * 1e-3) / 1e12
+    gbs = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
+    step_tflops = alg_flops / (ms_per_step * 1e-3) / 1e12
+    log(f"bench: {w.name}: {ms_per_step * 1e3:.1f} us/step, main kernel {kern_avg_ms * 1e3:.1f} us "
+        f"(min {min(kern_ms) * 1e3:.1f}), {tflops:.0f} TFLOP/s, {gbs:.0f} GB/s algorithmic")
+    traffic = measured_traffic(w.name, unq)
+    if unq:
+        # arithmetic intensity below the 16-bit ridge (flop per byte < 312.5): HBM binds
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "step_frac": alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "traffic": (traffic or {}).get("total_bytes"), "traffic_detail": traffic,
+                "kernel": "mla_decode_bf16_kernel", "kernel_avg_us": kern_avg_ms * 1e3,
+                "kernel_timed_launches": len(timed), "alg_flops_per_launch": alg_flops,
+                "alg_bytes_per_launch": alg_bytes, "alg_TFLOPs": tflops, "mfma_frac": tflops / PEAK_MFMA16_TFLOPS}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_MFMA16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_MFMA16_TFLOPS,
+                "step_frac": step_tflops / PEAK_MFMA16_TFLOPS,
+                "frac_note": "frac: main decode kernel alone (the dominant kernel); step_frac: the whole "
+                             "call (main kernel, split combine and launch gaps) per step",
+                "traffic": (traffic or {}).get("total_bytes"),
+                "traffic_detail": traffic,
+                "kernel": "mla_decode_kernel", "kernel_avg_us": kern_avg_ms * 1e3,
+                "kernel_timed_launches": len(timed),
+                "alg_flops_per_launch": alg_flops, "alg_bytes_per_launch": alg_bytes,
+                "alg_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+    return {"ms_per_step": ms_per_step, "kv_tokens": kv_tokens, "layers": len(layers), "plan": plan,
+            "roofline": roof, "after_main_us": 1e3 * sum(after_ms) / len(after_ms)}
 
 
 if __name__ == "__main__":

@@ -40,6 +40,15 @@
  *     cache_lengths[b] <= max_pages * page_size.  Table columns at or past
  *     ceil(cache_lengths[b] / page_size) are never read, so they may hold
  *     anything; so may unused slots, pages, layers and kv_dim entries.
+ *   - What the C layer can and cannot check: it receives raw pointers and an
+ *     mla_shape, so it validates the sizes, ranges, alignment and nullness
+ *     listed per entry point, but it cannot see element types, strides or the
+ *     tensors' own extents.  Element types, contiguous row-major layout, and
+ *     the agreement between tensors (scales dims 1..4 == blocks dims 1..4,
+ *     scales_lookup_table shape == lookup_table shape, out == [batch, q_len,
+ *     num_q_heads, 512], q's second dimension == q_len) are the caller's
+ *     contract; the Python binding checks them on the torch tensors before it
+ *     calls.  A C caller that breaks them gets undefined results.
  */
 #ifndef MLA_PAGED_H
 #define MLA_PAGED_H
@@ -52,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MLA_PAGED_ABI_VERSION 3
+#define MLA_PAGED_ABI_VERSION 4
 
 /* Status codes.  mla_status_string() returns a static description. */
 typedef enum {
@@ -165,6 +174,40 @@ mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, cons
                                          hipStream_t stream);
 
 /*
+ * mla_decode_paged_fp8_block_offsets — debug variant of
+ * mla_decode_paged_fp8_splits that also reports the page resolution the
+ * decode kernel itself computed for its loads ("generic_get_paged_cache_with_
+ * scales" page, "Args": lookup_table, scales_lookup_table).  The decode runs
+ * exactly as in mla_decode_paged_fp8_splits (same plan, same output); in
+ * addition, for every 16-key block k (keys 16k .. 16k+15) of request b that
+ * the kernel loads, it writes
+ *   block_offsets[b, k, 0] = byte offset of the block's first row,
+ *       LT[b, 16k / P] * page_stride + (16k % P) * head_dim
+ *   block_offsets[b, k, 1] = float offset of its first scale row,
+ *       SLT[b, 16k / P] * spage_stride + (16k % P) * scale_groups
+ * both counted from element (page 0, kv 0, layer_idx, slot 0, head 0, 0) of
+ * blocks / scales, with page_stride = kv_dim * num_layers * page_size *
+ * head_dim and spage_stride = kv_dim * num_layers * page_size * scale_groups.
+ * A block never straddles a page (page_size is a multiple of 16), so these
+ * two numbers fix the page, slot and scale page of all its 16 keys.  Blocks
+ * at or past ceil(L_b / 16) are not written.
+ *   block_offsets  device u64 [batch, max_blocks, 2] (written), 8-byte aligned
+ *   max_blocks     >= ceil(max_pages * page_size / 16), else MLA_ERR_SHAPE
+ * Other arguments, errors and ownership as for mla_decode_paged_fp8_splits;
+ * MLA_ERR_NULL when block_offsets is NULL.  For tests that check the index
+ * work bit for bit; not for production calls.
+ */
+mla_status mla_decode_paged_fp8_block_offsets(const void* q, const void* blocks, const float* scales,
+                                              const uint32_t* lookup_table,
+                                              const uint32_t* scales_lookup_table,
+                                              const uint32_t* cache_lengths, int32_t layer_idx,
+                                              int32_t q_len, float softmax_scale, void* out,
+                                              const mla_shape* shape, void* workspace,
+                                              size_t workspace_bytes, int32_t num_splits,
+                                              uint64_t* block_offsets, int32_t max_blocks,
+                                              hipStream_t stream);
+
+/*
  * mla_decode_paged_bf16 — the same attention over an unquantized paged cache.
  *
  * Quantization is a property of the cache type ("KVCacheScalesMHAOperand"
@@ -248,14 +291,15 @@ mla_status mla_decode_paged_fp8_plan(const mla_shape* shape, int32_t q_len,
                                      int32_t num_splits, mla_plan* plan);
 
 /*
- * mla_resolve_pages — debug view of page resolution, computed on the device
- * with the same routine the decode kernel uses for its tile addresses
- * (generic_get_paged_cache_with_scales page, "Args": lookup_table and
- * scales_lookup_table).  For b < batch and t < max_tokens writes
+ * mla_resolve_pages — per-token view of page resolution by a small debug
+ * kernel of its own (generic_get_paged_cache_with_scales page, "Args":
+ * lookup_table and scales_lookup_table).  It does not run the decode
+ * kernel's addressing code; mla_decode_paged_fp8_block_offsets reports that.
+ * For b < batch and t < max_tokens writes
  *   page[b, t]  = LT[b, t / page_size]   slot[b, t] = t % page_size
  *   spage[b, t] = SLT[b, t / page_size]  (SLT = LT when NULL)
- * for t < cache_lengths[b], and 0xFFFFFFFF in all three for t >= it.
- * Outputs are device u32 [batch, max_tokens].
+ * for t < min(cache_lengths[b], max_pages * page_size), and 0xFFFFFFFF in all
+ * three otherwise.  Outputs are device u32 [batch, max_tokens].
  */
 mla_status mla_resolve_pages(const uint32_t* lookup_table, const uint32_t* scales_lookup_table,
                              const uint32_t* cache_lengths, int32_t batch, int32_t max_pages,

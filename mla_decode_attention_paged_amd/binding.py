@@ -81,6 +81,8 @@ def load_library() -> ctypes.CDLL:
     lib.mla_decode_paged_fp8_splits.restype = ctypes.c_int
     lib.mla_decode_paged_fp8_profiled.argtypes = common + [ctypes.c_int32, vp, vp, vp]
     lib.mla_decode_paged_fp8_profiled.restype = ctypes.c_int
+    lib.mla_decode_paged_fp8_block_offsets.argtypes = common + [ctypes.c_int32, vp, ctypes.c_int32, vp]
+    lib.mla_decode_paged_fp8_block_offsets.restype = ctypes.c_int
     bf16_common = [vp, vp, u32p, u32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp,
                    ctypes.POINTER(MlaShape), vp, ctypes.c_size_t]
     lib.mla_decode_paged_bf16.argtypes = bf16_common + [vp]
@@ -142,9 +144,17 @@ def _check_tensor(name, t, dtypes, ndim, device):
         raise ValueError(f"{name}: on {t.device}, expected {device}")
 
 
-def _check_shapes(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, out):
+def _check_q_len(q, q_len):
+    """The kernels stride q and out by q_len rows per request: q_len must be q's
+    second dimension (a larger value would read past q and write past out)."""
+    if int(q_len) != q.shape[1]:
+        raise ValueError(f"q_len ({int(q_len)}) must equal q.shape[1] ({q.shape[1]})")
+
+
+def _check_shapes(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, out, q_len):
     """Cross-tensor shape checks that the C struct cannot express."""
     B = q.shape[0]
+    _check_q_len(q, q_len)
     if blocks.shape[1:5] != scales.shape[1:5]:
         raise ValueError("scales dims 1..4 must equal blocks dims 1..4")
     if blocks.shape[5] != q.shape[3]:
@@ -181,7 +191,7 @@ def workspace_bytes(q, blocks, scales, lookup_table, q_len, num_splits=0) -> int
 
 def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths,
                          layer_idx, q_len, softmax_scale, out=None, workspace=None, num_splits=None,
-                         main_events=None):
+                         main_events=None, block_offsets=None):
     """Decode attention over the paged FP8 cache; returns `out` (bf16 [B, q_len, H, 512]).
 
     q bf16 [B, q_len, H, 576]; blocks uint8 (E4M3FN bytes) [NB, KVD, NL, P, 1, 576];
@@ -192,6 +202,9 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
     num_splits: None for the automatic plan, or an explicit count.
     main_events: optional (begin, end) raw hipEvent_t handles recorded around
     the main kernel only (for timing it apart from the split combine).
+    block_offsets: optional int64 device tensor [B, max_blocks, 2] (debug): the
+    decode kernel writes the row and scale offsets it computed for every
+    16-key block it loads (mla_decode_paged_fp8_block_offsets in the C ABI).
     """
     lib = load_library()
     dev = q.device
@@ -207,7 +220,7 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
         _check_tensor("scales_lookup_table", scales_lookup_table, (torch.int32,), 2, dev)
     _check_tensor("cache_lengths", cache_lengths, (torch.int32,), 1, dev)
     _check_tensor("out", out, (torch.bfloat16,), 4, dev)
-    _check_shapes(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, out)
+    _check_shapes(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, out, q_len)
     shp = _shape(q, blocks, scales, lookup_table)
     want = 0 if num_splits is None else int(num_splits)
     if workspace is None:
@@ -218,7 +231,13 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
     args = (_ptr(q), _ptr(blocks), _ptr(scales), _ptr(lookup_table), _ptr(scales_lookup_table),
             _ptr(cache_lengths), int(layer_idx), int(q_len), float(softmax_scale), _ptr(out),
             ctypes.byref(shp), ws_ptr, ws_bytes)
-    if main_events is not None:
+    if block_offsets is not None:
+        if (block_offsets.dtype != torch.int64 or block_offsets.dim() != 3 or block_offsets.shape[0] != q.shape[0]
+                or block_offsets.shape[2] != 2 or not block_offsets.is_contiguous() or block_offsets.device != dev):
+            raise ValueError("block_offsets must be a contiguous int64 [B, max_blocks, 2] tensor on the device")
+        st = lib.mla_decode_paged_fp8_block_offsets(*args, want, _ptr(block_offsets), int(block_offsets.shape[1]),
+                                                    _stream_handle(dev))
+    elif main_events is not None:
         st = lib.mla_decode_paged_fp8_profiled(*args, want, ctypes.c_void_p(main_events[0]),
                                                ctypes.c_void_p(main_events[1]), _stream_handle(dev))
     elif num_splits is None:
@@ -251,6 +270,7 @@ def mla_decode_paged_bf16(q, blocks, lookup_table, cache_lengths, layer_idx, q_l
     _check_tensor("cache_lengths", cache_lengths, (torch.int32,), 1, dev)
     _check_tensor("out", out, (torch.bfloat16,), 4, dev)
     B = q.shape[0]
+    _check_q_len(q, q_len)
     if blocks.shape[5] != q.shape[3]:
         raise ValueError("head_dim of q and blocks differ")
     if lookup_table.shape[0] != B or cache_lengths.shape[0] != B:

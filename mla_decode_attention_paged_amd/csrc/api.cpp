@@ -117,7 +117,8 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
                        float softmax_scale, void* out, const mla_shape* shape, void* workspace,
                        size_t workspace_bytes, int32_t num_splits, bool explicit_splits,
                        hipStream_t stream, hipEvent_t main_begin = nullptr,
-                       hipEvent_t main_end = nullptr, bool unquantized = false) {
+                       hipEvent_t main_end = nullptr, bool unquantized = false,
+                       uint64_t* dbg_offsets = nullptr, int32_t dbg_blocks = 0) {
   if (!q || !blocks || (!unquantized && !scales) || !lookup_table || !cache_lengths || !out || !shape)
     return MLA_ERR_NULL;
   mla_status st = unquantized ? check_shape_unquantized(shape, q_len) : check_shape(shape, q_len);
@@ -175,6 +176,13 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
   a.lpt = (shape->batch > 1 && shape->batch <= mla::kLptMaxBatch &&
            (int64_t)shape->batch * plan.num_splits < 65536 && a.grid_units > device_cu_count()) ? 1 : 0;
   a.sm_log2 = softmax_scale * 1.4426950408889634f;
+  if (dbg_offsets) {
+    // one record per 16-key block the table width can address
+    if ((int64_t)dbg_blocks * 16 < (int64_t)shape->max_pages * shape->page_size) return MLA_ERR_SHAPE;
+    if (!aligned(dbg_offsets, 8)) return MLA_ERR_UNSUPPORTED;
+    a.dbg_offsets = dbg_offsets;
+    a.dbg_blocks = dbg_blocks;
+  }
 
   hipError_t e = unquantized ? mla::launch_decode_bf16(a, stream, main_begin, main_end)
                              : mla::launch_decode(a, shape->scale_groups, stream, main_begin, main_end);
@@ -219,6 +227,22 @@ mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, cons
   return decode_impl(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
                      q_len, softmax_scale, out, shape, workspace, workspace_bytes, num_splits,
                      num_splits > 0, stream, main_begin, main_end);
+}
+
+mla_status mla_decode_paged_fp8_block_offsets(const void* q, const void* blocks, const float* scales,
+                                              const uint32_t* lookup_table,
+                                              const uint32_t* scales_lookup_table,
+                                              const uint32_t* cache_lengths, int32_t layer_idx,
+                                              int32_t q_len, float softmax_scale, void* out,
+                                              const mla_shape* shape, void* workspace,
+                                              size_t workspace_bytes, int32_t num_splits,
+                                              uint64_t* block_offsets, int32_t max_blocks,
+                                              hipStream_t stream) {
+  if (!block_offsets) return MLA_ERR_NULL;
+  if (max_blocks <= 0) return MLA_ERR_SHAPE;
+  return decode_impl(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
+                     q_len, softmax_scale, out, shape, workspace, workspace_bytes, num_splits,
+                     num_splits > 0, stream, nullptr, nullptr, false, block_offsets, max_blocks);
 }
 
 mla_status mla_decode_paged_bf16(const void* q, const void* blocks, const uint32_t* lookup_table,

@@ -50,8 +50,10 @@ constexpr float kNegInf = -__builtin_inff();
 
 // ---------------------------------------------------------------- page resolution
 // Token t of request b: value page = LT[b, t / P], slot = t % P, scale page =
-// SLT[b, t / P] (SLT is LT when no separate table was given).  Shared by the
-// decode kernel's tile addressing and by the resolve debug kernel.
+// SLT[b, t / P] (SLT is LT when no separate table was given).  Used by the
+// resolve debug kernel; the decode kernel resolves whole 16-key blocks in its
+// page windows (fetch_window / enter_window) and can record what it computed
+// there (DecodeArgs::dbg_offsets).
 struct PageRef {
   uint32_t page, slot, spage;
 };
@@ -232,7 +234,10 @@ static_assert(Layout<1>::kTotal <= 160 * 1024 && Layout<9>::kTotal <= 160 * 1024
 static_assert(4 * kEpSlice * 4 <= 6 * kTileBytes, "epilogue transposes fit in the tile buffers");
 static_assert(2 * 2 * 18 * 64 * 16 <= 4 * kTileBytes, "q staging fits in the tile buffers of steps 1 and 2");
 
-template <int NG>
+// kRecord: also write the block offsets this kernel computes to a.dbg_offsets
+// (the debug entry point's instantiation; the production one carries no such
+// code, so that its registers are not spent on it).
+template <int NG, bool kRecord>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 mla_decode_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -358,12 +363,20 @@ mla_decode_kernel(DecodeArgs a) {
       const int bh = nvalid > 16 ? 1 : 0;           // block of the second half (clamped)
       const int kk = min(16 * hb + ld_key, nvalid - 1);
       const int half = __builtin_amdgcn_readfirstlane(min(hb, bh));   // half holding this wave's keys
-      dma_base = layer_base + lane_u64(w_off, blk0 + half);
+      const uint64_t row_off = lane_u64(w_off, blk0 + half);
+      dma_base = layer_base + row_off;
       dma_voff = (uint32_t)(kk - 16 * half) * kHeadDim + 16 * ld_col;
+      if (kRecord && lane == 0)
+        a.dbg_offsets[2 * ((size_t)b * a.dbg_blocks + (t0 >> 4) + half)] = row_off;
       if (hb == 0) {
         LDS_AS char* sdst = scale_buf(step, tt);
         const int key = min(lane & 31, nvalid - 1);
         const uint64_t so0 = lane_u64(w_soff, blk0), so1 = lane_u64(w_soff, blk0 + bh);
+        if (kRecord && lane == 0) {
+          uint64_t* rec = a.dbg_offsets + 2 * ((size_t)b * a.dbg_blocks + (t0 >> 4)) + 1;
+          rec[0] = so0;
+          if (bh) rec[2] = so1;
+        }
         const float* srow = slayer_base + ((key >> 4) ? so1 : so0) + (size_t)(key & 15) * NG;
         const uint32_t sd = (uint32_t)(uintptr_t)sdst;
         if constexpr (NG == 1) {
@@ -1043,7 +1056,8 @@ __global__ void mla_resolve_kernel(const uint32_t* lt, const uint32_t* slt, cons
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= batch || t >= max_tokens) return;
   const size_t o = (size_t)b * max_tokens + t;
-  if ((uint32_t)t < cache_lengths[b]) {
+  // tokens past what the table row can address are not resolved (as in decode)
+  if ((uint32_t)t < min(cache_lengths[b], (uint32_t)max_pages * (uint32_t)page_size)) {
     const PageRef r = resolve_token(lt, slt, max_pages, b, (uint32_t)t, (uint32_t)page_size);
     page[o] = r.page;
     slot[o] = r.slot;
@@ -1062,12 +1076,12 @@ size_t partial_bytes(int64_t batch, int64_t row_groups, int64_t num_splits) {
   return units * kRows * kVDim * sizeof(float) + units * kRows * sizeof(float);
 }
 
-template <int NG>
+template <int NG, bool kRecord>
 static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream, hipEvent_t begin, hipEvent_t end) {
   static bool attr_set = false;   // per process; the attribute is per function
   const int lds_bytes = Layout<NG>::kTotal;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)mla_decode_kernel<NG>,
+    hipError_t e = hipFuncSetAttribute((const void*)mla_decode_kernel<NG, kRecord>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -1075,10 +1089,10 @@ static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream, hipEvent_
   const int grid = decode_grid(a);
   if (begin && end) {
     // the events take the kernel's own start / end timestamps
-    hipExtLaunchKernelGGL(mla_decode_kernel<NG>, dim3(grid), dim3(kThreads), lds_bytes, stream,
+    hipExtLaunchKernelGGL((mla_decode_kernel<NG, kRecord>), dim3(grid), dim3(kThreads), lds_bytes, stream,
                           begin, end, 0, a);
   } else {
-    hipLaunchKernelGGL(mla_decode_kernel<NG>, dim3(grid), dim3(kThreads), lds_bytes, stream, a);
+    hipLaunchKernelGGL((mla_decode_kernel<NG, kRecord>), dim3(grid), dim3(kThreads), lds_bytes, stream, a);
   }
   return hipGetLastError();
 }
@@ -1088,8 +1102,12 @@ hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stre
   hipError_t e;
   const bool both = main_begin && main_end;
   if (main_begin && !both && (e = hipEventRecord(main_begin, stream)) != hipSuccess) return e;
-  e = scale_groups == 1 ? launch_main<1>(a, stream, main_begin, main_end)
-                        : launch_main<9>(a, stream, main_begin, main_end);
+  if (a.dbg_offsets)
+    e = scale_groups == 1 ? launch_main<1, true>(a, stream, main_begin, main_end)
+                          : launch_main<9, true>(a, stream, main_begin, main_end);
+  else
+    e = scale_groups == 1 ? launch_main<1, false>(a, stream, main_begin, main_end)
+                          : launch_main<9, false>(a, stream, main_begin, main_end);
   if (e != hipSuccess) return e;
   if (main_end && !both && (e = hipEventRecord(main_end, stream)) != hipSuccess) return e;
   if (a.num_splits > 1) e = launch_combine(a, stream);

@@ -44,6 +44,13 @@ struct DecodeArgs {
   int32_t grid_units;                // batch * row_groups * num_splits
   int32_t lpt;                       // 1: largest (request, split) key ranges first
   float sm_log2;                     // softmax_scale * log2(e)
+  // Debug record of the decode kernel's own page resolution (null in normal
+  // calls): for 16-key block k of request b, [b, k, 0] = byte offset of the
+  // block's first row from (page 0, kv 0, layer_idx, slot 0) and [b, k, 1] =
+  // float offset of its first scale row from the same place in scales, as
+  // the kernel computed them for its loads.  dbg_blocks = blocks per request.
+  uint64_t* dbg_offsets;
+  int32_t dbg_blocks;
 };
 
 size_t partial_bytes(int64_t batch, int64_t row_groups, int64_t num_splits);

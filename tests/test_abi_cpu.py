@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert binding.mla_abi_version() == 3
+    assert binding.mla_abi_version() == 4
     for code in range(7):
         assert lib.mla_status_string(code).decode()
     assert lib.mla_status_string(99).decode() == "unknown status"
@@ -229,3 +229,45 @@ def test_plan_two_waves_for_large_batches(lib):
     assert splits(4, 1024, P=128) == (32, 4096)
     assert splits(32, 16) == (4, 256)           # two waves would cut splits below 2048 keys
     assert splits(300, 16)[0] == 1              # more units than compute units already
+
+
+def test_block_offsets_entry_rejects_bad_args(lib):
+    """The debug entry with the decode kernel's own resolution record checks its
+    extra arguments on the host: a NULL record, a non-positive or too small
+    block count (one record per 16 keys of max_pages * page_size) and a
+    misaligned record are rejected before anything is launched."""
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(6)]
+    q, blocks, scales, lt, cl, out = fake
+    f = lib.mla_decode_paged_fp8_block_offsets
+
+    def go(rec, nblk, shape=None):
+        return f(q, blocks, scales, lt, None, cl, 0, 1, ctypes.c_float(0.07), out,
+                 ctypes.byref(shape or good_shape()), None, 0, 0, rec, nblk, None)
+    rec = ctypes.c_void_p(0x20000)
+    assert go(None, 64) == NULL
+    assert go(rec, 0) == SHAPE
+    assert go(rec, 31) == SHAPE                      # 8 pages x 64 keys = 512 keys = 32 blocks
+    assert go(ctypes.c_void_p(0x20004), 32) == UNSUP
+    assert go(rec, 32, good_shape(batch=0)) == SHAPE
+
+
+def test_binding_checks_q_len_against_q():
+    """The kernels stride q and out by q_len rows per request, so the binding
+    refuses a q_len that differs from q's second dimension (on meta tensors:
+    no device is needed and nothing is launched)."""
+    import torch
+    meta = torch.device("meta")
+    q = torch.empty((2, 4, 128, 576), dtype=torch.bfloat16, device=meta)
+    blocks = torch.empty((8, 1, 1, 64, 1, 576), dtype=torch.uint8, device=meta)
+    scales = torch.empty((8, 1, 1, 64, 1, 1), dtype=torch.float32, device=meta)
+    lt = torch.empty((2, 4), dtype=torch.int32, device=meta)
+    cl = torch.empty((2,), dtype=torch.int32, device=meta)
+    out = torch.empty((2, 4, 128, 512), dtype=torch.bfloat16, device=meta)
+    binding._check_shapes(q, blocks, scales, lt, None, cl, out, 4)
+    for bad in (1, 3, 5):
+        with pytest.raises(ValueError, match="q_len"):
+            binding._check_shapes(q, blocks, scales, lt, None, cl, out, bad)
+    with pytest.raises(ValueError, match="scales dims"):
+        binding._check_shapes(q, blocks, scales[:, :, :, :32], lt, None, cl, out, 4)
+    with pytest.raises(ValueError, match="scales_lookup_table"):
+        binding._check_shapes(q, blocks, scales, lt, lt[:, :2], cl, out, 4)

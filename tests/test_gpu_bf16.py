@@ -101,7 +101,8 @@ def test_q4_rows_equal_q1_calls(gpu_device):
 
 def test_split_partials_beyond_f16_range(gpu_device):
     """Cache rows x 2^14 and q x 2^-14: the same scores, O x 2^14, past f16's
-    range; the f16 split partials carry a power-of-two factor per row."""
+    largest finite value; the fp32 split partials and the combine must carry
+    such outputs, and P (bf16 hi + lo) must stay exact enough at that scale."""
     say("bf16 cache, partials beyond the f16 range")
     w = _w(gpu_device, 2, 128, [3000, 700], 64, 576, seed=74, poison=True, kv_dtype="bf16")
     w.blocks.mul_(2.0 ** 14)

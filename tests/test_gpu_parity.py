@@ -15,7 +15,7 @@ import torch
 from mla_decode_attention_paged_amd import mla_resolve_pages
 from mla_decode_attention_paged_amd.synth import make_workload, tiny, u32_numpy
 from oracle import resolve
-from tests.gpu_helpers import check_gate, run_gpu, say
+from tests.gpu_helpers import check_block_offsets, check_gate, run_gpu, say
 from tests.oracle_inputs import oracle_decode
 
 pytestmark = pytest.mark.gpu
@@ -45,6 +45,23 @@ def test_resolve_bit_exact(gpu_device, page, indep, lengths):
         for k in range(3):
             assert np.array_equal(got[k][b, :L].astype(np.int64), rows[b][:, k]), (b, k)
             assert (got[k][b, L:] == 0xFFFFFFFF).all()
+
+
+@pytest.mark.parametrize("page,gran,indep,splits", [
+    (16, 576, False, 1), (16, 64, True, None), (64, 576, True, 3), (64, 64, False, None),
+    (128, 576, False, None), (128, 64, True, 2),
+])
+def test_kernel_resolution_bit_exact(gpu_device, page, gran, indep, splits):
+    """The decode kernel's own page and scale-page resolution (the offsets it
+    loads from), recorded by the kernel itself, equals the oracle's resolution
+    bit for bit; layer 1 of 3 selected; ragged lengths across pages and
+    windows of 64 blocks; unused table columns hold 0xFFFFFFFF."""
+    say("kernel resolution", page, gran, indep, splits)
+    w = _w(gpu_device, 4, 128, [1, 16 * page + 5, 33, 70 * 16 + 3], page, gran, num_layers=3, layer_idx=1,
+           independent_scales=indep, spare_blocks=3, spare_scale_blocks=4, unused_table_id=0xFFFFFFFF,
+           seed=100 + page + gran, poison=True)
+    out = check_block_offsets(w, num_splits=splits, what=f"P{page} G{gran} indep={indep} splits={splits}")
+    check_gate(out, oracle_decode(w), "kernel resolution output")
 
 
 # ------------------------------------------------------------------ parity, small
@@ -206,21 +223,28 @@ def test_q4_rows_equal_q1_calls(gpu_device, gran):
     _q1_calls_match_q4_rows(w, run_gpu)
 
 
-def test_split_partials_beyond_f16_range(gpu_device):
-    """Split partials are stored in f16 with a power-of-two factor per row
-    quarter: outputs far past f16's largest finite value (65504) must still
-    merge correctly.  Scales x 2^14 and q x 2^-14 leave every score unchanged
-    and multiply O by 2^14 exactly (powers of two)."""
-    say("partials beyond the f16 range")
-    w = _w(gpu_device, 2, 128, [3000, 700], 64, 576, seed=73, poison=True)
-    w.scales.mul_(2.0 ** 14)
-    w.q.mul_(2.0 ** -14)
+@pytest.mark.parametrize("gran,e", [(576, 14), (64, 11)])
+def test_split_partials_beyond_f16_range(gpu_device, gran, e):
+    """Large scales: scales x 2^e and q x 2^-e leave every score unchanged and
+    multiply O by 2^e exactly (powers of two).  With per-token scales (e = 14)
+    the outputs pass f16's largest finite value (65504): the fp32 split
+    partials and the combine must carry them, and the per-tile threshold
+    must keep P' = p * s finite in f16.  With group scales (e = 11) the scales
+    reach the range where P' = p * s_g depends on the threshold's bound
+    p <= 2^8 (the documented contract is s_g <= 255)."""
+    say("large scales", gran, e)
+    w = _w(gpu_device, 2, 128, [3000, 700], 64, gran, independent_scales=gran == 64, seed=73, poison=True)
+    w.scales.mul_(2.0 ** e)
+    w.q.mul_(2.0 ** -e)
     ref = oracle_decode(w)
-    assert np.abs(ref).max() > 65504.0
-    # the gate is read at the unscaled magnitudes (division by 2^14 is exact)
+    if gran == 576:
+        assert np.abs(ref).max() > 65504.0
+    else:
+        assert 64.0 < float(w.scales[torch.isfinite(w.scales)].max()) <= 255.0
+    # the gate is read at the unscaled magnitudes (division by 2^e is exact)
     for splits in (1, 2, 7):
-        out = run_gpu(w, num_splits=splits).to(torch.float64) * 2.0 ** -14
-        check_gate(out, ref * 2.0 ** -14, f"x2^14 splits {splits}")
+        out = run_gpu(w, num_splits=splits).to(torch.float64) * 2.0 ** -e
+        check_gate(out, ref * 2.0 ** -e, f"G{gran} x2^{e} splits {splits}")
 
 
 @pytest.mark.parametrize("splits", [24, 40, 157])
