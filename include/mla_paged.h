@@ -208,6 +208,38 @@ mla_status mla_decode_paged_fp8_block_offsets(const void* q, const void* blocks,
                                               hipStream_t stream);
 
 /*
+ * mla_decode_paged_fp8_noalloc — mla_decode_paged_fp8 for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and result as
+ * mla_decode_paged_fp8_splits without the workspace: the split partials go to
+ * a device array inside the library, mla_noalloc_scratch_bytes() bytes
+ * (64 MiB) per GPU, resolved on the first call on each device and held until
+ * the process ends.  The call itself allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine).
+ *   num_splits  0: the automatic plan, limited to what the scratch holds
+ *               (fewer splits, or none, for very large batches); > 0: that
+ *               split count, rejected with MLA_ERR_WORKSPACE when its
+ *               partials (mla_decode_paged_fp8_plan's workspace_bytes)
+ *               exceed the scratch.
+ * Every call on one GPU uses that GPU's one scratch array: calls that overlap
+ * in time on the same GPU (different streams, or host threads) race and must
+ * be serialized by the caller.  The scratch needs no clearing: a call writes
+ * every partial it reads.  Errors as for mla_decode_paged_fp8_splits, all
+ * checked on the host before any HIP call; MLA_ERR_HIP when the scratch's
+ * device address cannot be obtained.
+ */
+mla_status mla_decode_paged_fp8_noalloc(const void* q, const void* blocks, const float* scales,
+                                        const uint32_t* lookup_table,
+                                        const uint32_t* scales_lookup_table,
+                                        const uint32_t* cache_lengths, int32_t layer_idx,
+                                        int32_t q_len, float softmax_scale, void* out,
+                                        const mla_shape* shape, int32_t num_splits,
+                                        hipStream_t stream);
+
+/* Bytes of the per-GPU split scratch of mla_decode_paged_fp8_noalloc. */
+size_t mla_noalloc_scratch_bytes(void);
+
+/*
  * mla_decode_paged_bf16 — the same attention over an unquantized paged cache.
  *
  * Quantization is a property of the cache type ("KVCacheScalesMHAOperand"

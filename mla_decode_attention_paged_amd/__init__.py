@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     mla_append_kv_fp8,
     mla_decode_paged_bf16,
     mla_decode_paged_fp8,
+    mla_decode_paged_fp8_noalloc,
     mla_decode_paged_fp8_plan,
     mla_resolve_pages,
     workspace_bytes,

@@ -81,6 +81,11 @@ def load_library() -> ctypes.CDLL:
     lib.mla_decode_paged_fp8_splits.restype = ctypes.c_int
     lib.mla_decode_paged_fp8_profiled.argtypes = common + [ctypes.c_int32, vp, vp, vp]
     lib.mla_decode_paged_fp8_profiled.restype = ctypes.c_int
+    lib.mla_decode_paged_fp8_noalloc.argtypes = [vp, vp, f32p, u32p, u32p, u32p, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_float, vp, ctypes.POINTER(MlaShape), ctypes.c_int32, vp]
+    lib.mla_decode_paged_fp8_noalloc.restype = ctypes.c_int
+    lib.mla_noalloc_scratch_bytes.argtypes = []
+    lib.mla_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.mla_decode_paged_fp8_block_offsets.argtypes = common + [ctypes.c_int32, vp, ctypes.c_int32, vp]
     lib.mla_decode_paged_fp8_block_offsets.restype = ctypes.c_int
     bf16_common = [vp, vp, u32p, u32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp,
@@ -246,6 +251,35 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
         st = lib.mla_decode_paged_fp8_splits(*args, int(num_splits), _stream_handle(dev))
     if st != MLA_OK:
         raise MlaError(st, "mla_decode_paged_fp8")
+    return out
+
+
+def mla_decode_paged_fp8_noalloc(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths,
+                                 layer_idx, q_len, softmax_scale, out, num_splits=0):
+    """mla_decode_paged_fp8 through the entry point that allocates nothing: the
+    split partials use the library's per-GPU scratch.  `out` (bf16 [B, q_len, H,
+    512]) must be given; nothing is allocated here either.  num_splits 0 picks
+    the automatic plan within the scratch."""
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("mla_decode_paged_fp8_noalloc runs on the GPU only; got tensors on " + str(dev))
+    _check_tensor("q", q, (torch.bfloat16,), 4, dev)
+    _check_tensor("blocks", blocks, (torch.uint8, torch.float8_e4m3fn), 6, dev)
+    _check_tensor("scales", scales, (torch.float32,), 6, dev)
+    _check_tensor("lookup_table", lookup_table, (torch.int32,), 2, dev)
+    if scales_lookup_table is not None:
+        _check_tensor("scales_lookup_table", scales_lookup_table, (torch.int32,), 2, dev)
+    _check_tensor("cache_lengths", cache_lengths, (torch.int32,), 1, dev)
+    _check_tensor("out", out, (torch.bfloat16,), 4, dev)
+    _check_shapes(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, out, q_len)
+    shp = _shape(q, blocks, scales, lookup_table)
+    st = lib.mla_decode_paged_fp8_noalloc(_ptr(q), _ptr(blocks), _ptr(scales), _ptr(lookup_table),
+                                          _ptr(scales_lookup_table), _ptr(cache_lengths), int(layer_idx),
+                                          int(q_len), float(softmax_scale), _ptr(out), ctypes.byref(shp),
+                                          int(num_splits), _stream_handle(dev))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_decode_paged_fp8_noalloc")
     return out
 
 

@@ -4,7 +4,8 @@
 
 Compiles csrc/mla_decode.hip (FP8 decode kernels + launchers),
 csrc/mla_decode_bf16.hip (unquantized-cache decode kernel), csrc/kv_append.hip
-(append-and-quantise kernel) and csrc/api.cpp (C ABI) into
+(append-and-quantise kernel), csrc/noalloc.hip (the decode entry point with a
+device-resident split scratch) and csrc/api.cpp (C ABI) into
 mla_decode_attention_paged_amd/libmla_paged.so.  Packed-FP32 VALU
 instructions are disabled for the device code.
 """
@@ -48,7 +49,7 @@ def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="mla_build_") as tmp:
         objs = []
         for src, lang in (("mla_decode.hip", "hip"), ("mla_decode_bf16.hip", "hip"), ("kv_append.hip", "hip"),
-                          ("api.cpp", "c++")):
+                          ("noalloc.hip", "hip"), ("api.cpp", "c++")):
             obj = os.path.join(tmp, src + ".o")
             cmd = [hipcc, *device_flags(), "-x", lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if lang == "c++":

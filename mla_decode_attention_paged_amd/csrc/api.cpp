@@ -109,6 +109,25 @@ mla_status check_shape_unquantized(const mla_shape* s, int32_t q_len) {
   return check_shape(&t, q_len);
 }
 
+// Pointers, sizes, ranges and alignment of a decode call (host only).
+mla_status check_args(const void* q, const void* blocks, const float* scales, const uint32_t* lookup_table,
+                      const uint32_t* scales_lookup_table, const uint32_t* cache_lengths, int32_t layer_idx,
+                      int32_t q_len, float softmax_scale, const void* out, const mla_shape* shape,
+                      int32_t num_splits, bool unquantized) {
+  if (!q || !blocks || (!unquantized && !scales) || !lookup_table || !cache_lengths || !out || !shape)
+    return MLA_ERR_NULL;
+  mla_status st = unquantized ? check_shape_unquantized(shape, q_len) : check_shape(shape, q_len);
+  if (st != MLA_OK) return st;
+  if (layer_idx < 0 || layer_idx >= shape->num_layers) return MLA_ERR_RANGE;
+  if (num_splits < 0) return MLA_ERR_RANGE;
+  if (!isfinite(softmax_scale) || softmax_scale <= 0.0f) return MLA_ERR_RANGE;
+  if (!aligned(q, 16) || !aligned(blocks, 16) || !aligned(out, 16) ||
+      (!unquantized && !aligned(scales, 4)) || !aligned(lookup_table, 4) ||
+      (scales_lookup_table && !aligned(scales_lookup_table, 4)) || !aligned(cache_lengths, 4))
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
 // unquantized: blocks hold bf16 rows and there are no scales (scales and
 // scales_lookup_table are ignored).
 mla_status decode_impl(const void* q, const void* blocks, const float* scales,
@@ -119,17 +138,10 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
                        hipStream_t stream, hipEvent_t main_begin = nullptr,
                        hipEvent_t main_end = nullptr, bool unquantized = false,
                        uint64_t* dbg_offsets = nullptr, int32_t dbg_blocks = 0) {
-  if (!q || !blocks || (!unquantized && !scales) || !lookup_table || !cache_lengths || !out || !shape)
-    return MLA_ERR_NULL;
-  mla_status st = unquantized ? check_shape_unquantized(shape, q_len) : check_shape(shape, q_len);
+  mla_status st = check_args(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
+                             q_len, softmax_scale, out, shape, num_splits, unquantized);
   if (st != MLA_OK) return st;
-  if (layer_idx < 0 || layer_idx >= shape->num_layers) return MLA_ERR_RANGE;
-  if (num_splits < 0) return MLA_ERR_RANGE;
-  if (!isfinite(softmax_scale) || softmax_scale <= 0.0f) return MLA_ERR_RANGE;
-  if (!aligned(q, 16) || !aligned(blocks, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
-      (!unquantized && !aligned(scales, 4)) || !aligned(lookup_table, 4) ||
-      (scales_lookup_table && !aligned(scales_lookup_table, 4)) || !aligned(cache_lengths, 4))
-    return MLA_ERR_UNSUPPORTED;
+  if (!aligned(workspace, 16)) return MLA_ERR_UNSUPPORTED;
 
   mla_plan plan;
   if (explicit_splits && num_splits > 0) {
@@ -190,6 +202,42 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
 }
 
 }  // namespace
+
+namespace mla {
+// The decode entry with an explicit workspace, for the entry points defined in
+// other source files of the library (noalloc.hip).
+mla_status decode_with_workspace(const void* q, const void* blocks, const float* scales,
+                                 const uint32_t* lookup_table, const uint32_t* scales_lookup_table,
+                                 const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                                 float softmax_scale, void* out, const mla_shape* shape, void* workspace,
+                                 size_t workspace_bytes, int32_t num_splits, hipStream_t stream) {
+  return decode_impl(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
+                     q_len, softmax_scale, out, shape, workspace, workspace_bytes, num_splits,
+                     num_splits > 0, stream);
+}
+
+mla_status check_decode_args(const void* q, const void* blocks, const float* scales,
+                             const uint32_t* lookup_table, const uint32_t* scales_lookup_table,
+                             const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                             float softmax_scale, const void* out, const mla_shape* shape,
+                             int32_t num_splits) {
+  return check_args(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx, q_len,
+                    softmax_scale, out, shape, num_splits, false);
+}
+
+// Workspace bytes the plan for these sizes needs (0: unsplit), or a status.
+mla_status plan_workspace(const mla_shape* shape, int32_t q_len, int32_t num_splits, size_t ws_limit,
+                          size_t* bytes) {
+  mla_plan p;
+  mla_status st = check_shape(shape, q_len);
+  if (st != MLA_OK) return st;
+  if (num_splits < 0) return MLA_ERR_RANGE;
+  st = make_plan(shape, q_len, num_splits, ws_limit, num_splits == 0, &p);
+  if (st != MLA_OK) return st;
+  *bytes = p.workspace_bytes;
+  return MLA_OK;
+}
+}  // namespace mla
 
 extern "C" {
 

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
+#include "mla_paged.h"
+
 namespace mla {
 
 constexpr int kHeadDim = 576;            // latent key depth (512 value dims + 64 rope dims)
@@ -85,6 +87,24 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, hipEvent_
 // The split combine alone (mla_decode.hip): merges the fp32 partials in a.ws_o /
 // a.ws_lse into a.out.
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
+
+// The decode with a caller-given workspace (api.cpp), for other entry points.
+mla_status decode_with_workspace(const void* q, const void* blocks, const float* scales,
+                                 const uint32_t* lookup_table, const uint32_t* scales_lookup_table,
+                                 const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                                 float softmax_scale, void* out, const mla_shape* shape, void* workspace,
+                                 size_t workspace_bytes, int32_t num_splits, hipStream_t stream);
+// Host checks of a decode call's arguments (pointers, sizes, ranges,
+// alignment), as every FP8 decode entry point makes them before any HIP call.
+mla_status check_decode_args(const void* q, const void* blocks, const float* scales,
+                             const uint32_t* lookup_table, const uint32_t* scales_lookup_table,
+                             const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                             float softmax_scale, const void* out, const mla_shape* shape,
+                             int32_t num_splits);
+// Workspace bytes of the plan for these sizes: the automatic plan (num_splits
+// 0) limited to ws_limit bytes, or the explicit split count's (unlimited).
+mla_status plan_workspace(const mla_shape* shape, int32_t q_len, int32_t num_splits, size_t ws_limit,
+                          size_t* bytes);
 
 hipError_t launch_resolve(const uint32_t* lt, const uint32_t* slt, const uint32_t* cache_lengths,
                           int batch, int max_pages, int page_size, int max_tokens,
