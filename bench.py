@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload uniform]
 
-A step is one decode call (main kernel + split combine when the plan splits)
-over one layer of a resident multi-layer paged FP8 cache.  Consecutive steps
+A step is one decode call (one launch: the decode workgroups, and the split
+merge workgroups when the plan splits) over one layer of a resident multi-layer paged FP8 cache.  Consecutive steps
 decode consecutive layers, as a model's per-layer calls do; the cache holds
 enough layers (>= 512 MiB) that no step finds its layer in the 256 MB
 Infinity Cache.  Inputs are drawn once (synthetic, seeded) and stay in HBM.
@@ -34,6 +34,7 @@ WORKLOADS = ("uniform", "ragged", "long1", "long4", "spec", "chunk", "tiny")
 KERNEL_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "mla_decode.hip")
 KERNEL_SRC_BF16 = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "mla_decode_bf16.hip")
 UNIT_ORDER_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "unit_order.h")
+SPLIT_MERGE_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "split_merge.h")
 
 # HBM traffic of one main-kernel launch, from two rocprofv3 --pmc runs of
 # `bench.py --steps 5 --warmup 2 --no-cpu-baseline` (FETCH_SIZE, then
@@ -168,7 +169,7 @@ class HipEvents:
 def kernel_digest(unquantized=False):
     """SHA-256 of the device code in the kernel source (everything between the
     first device helper and the host launchers) and of the shared unit
-    mapping (unit_order.h)."""
+    mapping (unit_order.h) and split merge (split_merge.h)."""
     import hashlib
     path = KERNEL_SRC_BF16 if unquantized else KERNEL_SRC
     with open(path, "r") as f:
@@ -181,7 +182,9 @@ def kernel_digest(unquantized=False):
         b = src.index("// ---------------------------------------------------------------- host launchers")
     with open(UNIT_ORDER_SRC, "r") as f:       # the workgroup -> unit mapping both kernels use
         order = f.read()
-    return hashlib.sha256((src[a:b] + order).encode()).hexdigest()
+    with open(SPLIT_MERGE_SRC, "r") as f:
+        merge = f.read()
+    return hashlib.sha256((src[a:b] + order + merge).encode()).hexdigest()
 
 
 def measured_traffic(workload, unquantized=False):
@@ -378,7 +381,7 @@ def time_decode(w, steps, warmup, splits, event_every, unq):
     returns the step rate, the main kernel's own time and the roofline record."""
     import torch
     from mla_decode_attention_paged_amd import (mla_decode_paged_bf16, mla_decode_paged_fp8,
-                                                mla_decode_paged_fp8_plan)
+                                                mla_decode_paged_fp8_plan, new_workspace)
     dev = w.q.device
     w, layers = replicate_layers(w, 2 * MALL_BYTES)
     alg_bytes, alg_flops, kv_tokens = algorithmic(w)
@@ -387,7 +390,7 @@ def time_decode(w, steps, warmup, splits, event_every, unq):
                                      tuple(w.lookup_table.shape), w.q_len, splits or 0)
     log(f"bench: {w.name}: layers {len(layers)}, plan {plan}, kv tokens/step {kv_tokens}")
     out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+    ws = new_workspace(plan["workspace_bytes"], dev)   # allocated and its counters zeroed once
     every = max(1, event_every)
     timed = [i for i in range(steps) if i % every == 0]
     ev = HipEvents(len(timed))
@@ -417,7 +420,8 @@ def time_decode(w, steps, warmup, splits, event_every, unq):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
     kern_ms = [ev.elapsed_ms(k) for k in range(len(timed))]
-    # main kernel end -> the call's last work on the stream (split combine and launch gap)
+    # decode launch end -> the call's last work on the stream (nothing else is
+    # launched since the split merge joined the decode launch: the gap only)
     after_ms = [ev.elapsed_to_torch_event_ms(k, after[k]) for k in range(len(timed))]
     ev.close()
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
@@ -439,8 +443,8 @@ def time_decode(w, steps, warmup, splits, event_every, unq):
         roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_MFMA16_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_MFMA16_TFLOPS,
                 "step_frac": step_tflops / PEAK_MFMA16_TFLOPS,
-                "frac_note": "frac: main decode kernel alone (the dominant kernel); step_frac: the whole "
-                             "call (main kernel, split combine and launch gaps) per step",
+                "frac_note": "frac: the decode launch (its split merge included); step_frac: the whole "
+                             "call per step, launch gaps included",
                 "traffic": (traffic or {}).get("total_bytes"),
                 "traffic_detail": traffic,
                 "kernel": "mla_decode_kernel", "kernel_avg_us": kern_avg_ms * 1e3,

@@ -26,8 +26,10 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers to contiguous row-major
  *     buffers with the shapes given below; the caller owns them.  The
- *     library allocates no device memory, keeps no pointer after a call
- *     returns, and holds no state between calls (reentrant).
+ *     library allocates no device memory and keeps no pointer after a call
+ *     returns.  The only state that outlives a call is the split completion
+ *     flags at the start of a workspace, which every call returns to
+ *     zero (see mla_decode_paged_fp8, workspace).
  *   - Work is enqueued asynchronously on `stream`; inputs must stay alive
  *     and unmodified until the stream has passed the call.
  *   - Arguments are validated on the host before any HIP call.  On any
@@ -61,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MLA_PAGED_ABI_VERSION 4
+#define MLA_PAGED_ABI_VERSION 5
 
 /* Status codes.  mla_status_string() returns a static description. */
 typedef enum {
@@ -108,12 +110,14 @@ typedef struct {
   int32_t row_groups;        /* ceil(q_len * num_q_heads / 32)                     */
   int32_t num_splits;        /* key-range splits per (request, row group)          */
   int32_t tokens_per_split;  /* keys per split, a multiple of 128                  */
-  int32_t grid;              /* workgroups of the main kernel in request order; with
-                                more workgroups than compute units (batch <= 256) the
-                                FP8 kernel deals (request, split) key ranges largest
+  int32_t grid;              /* decode workgroups in request order; with more
+                                workgroups than compute units (batch <= 256) the
+                                kernels deal (request, split) key ranges largest
                                 first and may launch up to 8 * ceil(q_len * heads / 64)
-                                more, which exit at once                          */
-  size_t workspace_bytes;    /* split partials; 0 when num_splits == 1             */
+                                more, which exit at once.  With num_splits > 1 the
+                                same launch adds the split-merge workgroups      */
+  size_t workspace_bytes;    /* split flags (288 KiB) + partials; 0 when
+                                num_splits == 1                                  */
 } mla_plan;
 
 /*
@@ -130,10 +134,21 @@ typedef struct {
  * tokens are the queries themselves, causal among each other).  A row with
  * no visible key yields zeros.
  *
- * workspace: device buffer for split partials, or NULL.  With NULL (or too
+ * workspace: device buffer for a split plan, or NULL.  With NULL (or too
  * small to hold any split plan) the call runs unsplit, which is always
  * correct.  Use mla_decode_paged_fp8_plan() to learn the size that the
- * automatic plan wants.  q values must satisfy |q| <= 65504.
+ * automatic plan wants.  Layout: 288 KiB of split completion flags, then
+ * the fp32 partials.  The flags must be ZERO before a buffer's first use
+ * as a workspace (e.g. hipMemset once after allocating it); every call that
+ * splits returns them to zero, so the same workspace serves any later call,
+ * of any shape, with no clearing in between (also under graph replay).
+ * Calls that share a workspace must not overlap in time (one stream, or
+ * caller-side ordering); a workspace whose flags are not zero makes the
+ * split merge wait (bounded, about half a second) and write NaN rows.
+ * Split plans serve at most 8192 (request, row-group pair) units (larger
+ * batches run unsplit), at most 4096 splits, and at most 65536 (pair,
+ * split) units (the automatic plan takes fewer splits).  q values must
+ * satisfy |q| <= 65504.
  */
 mla_status mla_decode_paged_fp8(const void* q, const void* blocks, const float* scales,
                                 const uint32_t* lookup_table,
@@ -146,7 +161,9 @@ mla_status mla_decode_paged_fp8(const void* q, const void* blocks, const float* 
 /* Same as mla_decode_paged_fp8 with an explicit split count (0 = automatic).
  * An explicit count needs a workspace of at least plan.workspace_bytes
  * (MLA_ERR_WORKSPACE otherwise); num_splits is clamped to the number of
- * 128-key chunks of max_pages * page_size. */
+ * 128-key chunks of max_pages * page_size and to 4096.  A count > 1 for more
+ * than 8192 (request, row-group pair) units, or whose (pair, split) units
+ * exceed 65536, is refused with MLA_ERR_UNSUPPORTED. */
 mla_status mla_decode_paged_fp8_splits(const void* q, const void* blocks, const float* scales,
                                        const uint32_t* lookup_table,
                                        const uint32_t* scales_lookup_table,
@@ -156,8 +173,8 @@ mla_status mla_decode_paged_fp8_splits(const void* q, const void* blocks, const 
                                        size_t workspace_bytes, int32_t num_splits,
                                        hipStream_t stream);
 
-/* Same as mla_decode_paged_fp8_splits, and additionally times the main decode
- * kernel alone (not the split combine): when both `main_begin` and `main_end`
+/* Same as mla_decode_paged_fp8_splits, and additionally times the decode
+ * launch (the one kernel, its split merge included): when both `main_begin` and `main_end`
  * (caller-created HIP events) are given, the kernel is launched with
  * hipExtLaunchKernel so that the events carry its own start and end
  * timestamps; when only one is given it is recorded on `stream` right before
@@ -223,8 +240,10 @@ mla_status mla_decode_paged_fp8_block_offsets(const void* q, const void* blocks,
  *               exceed the scratch.
  * Every call on one GPU uses that GPU's one scratch array: calls that overlap
  * in time on the same GPU (different streams, or host threads) race and must
- * be serialized by the caller.  The scratch needs no clearing: a call writes
- * every partial it reads.  Errors as for mla_decode_paged_fp8_splits, all
+ * be serialized by the caller.  The scratch needs no clearing: its split
+ * flags start at zero (the array is zero-initialized when the library is
+ * loaded) and every call returns them to zero, and a call writes every
+ * partial it reads.  Errors as for mla_decode_paged_fp8_splits, all
  * checked on the host before any HIP call; MLA_ERR_HIP when the scratch's
  * device address cannot be obtained.
  */

@@ -17,5 +17,6 @@ from .binding import (  # noqa: F401
     mla_decode_paged_fp8_noalloc,
     mla_decode_paged_fp8_plan,
     mla_resolve_pages,
+    new_workspace,
     workspace_bytes,
 )

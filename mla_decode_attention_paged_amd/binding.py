@@ -189,6 +189,18 @@ def mla_decode_paged_fp8_plan(q_shape, blocks_shape, scales_shape, lookup_shape,
             "workspace_bytes": int(plan.workspace_bytes)}
 
 
+# Bytes of split completion counters at the start of every split workspace.
+SPLIT_FLAG_BYTES = 288 * 1024
+
+
+def new_workspace(nbytes, device):
+    """A device workspace of nbytes (uint8) whose split counters are zero, as
+    the library needs before a buffer's first use; later calls keep them zero."""
+    ws = torch.empty(max(int(nbytes), SPLIT_FLAG_BYTES), dtype=torch.uint8, device=device)
+    ws[:SPLIT_FLAG_BYTES].zero_()
+    return ws
+
+
 def workspace_bytes(q, blocks, scales, lookup_table, q_len, num_splits=0) -> int:
     return mla_decode_paged_fp8_plan(tuple(q.shape), tuple(blocks.shape), tuple(scales.shape),
                                      tuple(lookup_table.shape), q_len, num_splits)["workspace_bytes"]
@@ -203,10 +215,11 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
     scales float32 [NBs, KVD, NL, P, 1, 576 / granularity]; lookup_table and
     scales_lookup_table (or None) uint32 ids stored in int32 tensors [B, max_pages];
     cache_lengths uint32 in an int32 tensor [B].  workspace: a uint8 device
-    tensor for split partials, or None to have one allocated per the plan.
+    tensor from new_workspace() (its split counters zeroed once; every call
+    leaves them zero), or None to have one allocated per the plan.
     num_splits: None for the automatic plan, or an explicit count.
-    main_events: optional (begin, end) raw hipEvent_t handles recorded around
-    the main kernel only (for timing it apart from the split combine).
+    main_events: optional (begin, end) raw hipEvent_t handles that take the
+    decode launch's own start and end timestamps.
     block_offsets: optional int64 device tensor [B, max_blocks, 2] (debug): the
     decode kernel writes the row and scale offsets it computed for every
     16-key block it loads (mla_decode_paged_fp8_block_offsets in the C ABI).
@@ -230,7 +243,7 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
     want = 0 if num_splits is None else int(num_splits)
     if workspace is None:
         need = workspace_bytes(q, blocks, scales, lookup_table, q_len, want)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need > 0 else None
+        workspace = new_workspace(need, dev) if need > 0 else None
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(q), _ptr(blocks), _ptr(scales), _ptr(lookup_table), _ptr(scales_lookup_table),
@@ -319,7 +332,7 @@ def mla_decode_paged_bf16(q, blocks, lookup_table, cache_lengths, layer_idx, q_l
     if workspace is None:
         need = mla_decode_paged_fp8_plan(tuple(q.shape), tuple(blocks.shape), (1, KVD, NL, P, HKV, 1),
                                          tuple(lookup_table.shape), q_len, want)["workspace_bytes"]
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+        workspace = new_workspace(need, dev) if need > 0 else None
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(q), _ptr(blocks), _ptr(lookup_table), _ptr(cache_lengths), int(layer_idx), int(q_len),

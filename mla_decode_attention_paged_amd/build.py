@@ -2,7 +2,8 @@
 
     python -m mla_decode_attention_paged_amd.build
 
-Compiles csrc/mla_decode.hip (FP8 decode kernels + launchers),
+Compiles csrc/mla_decode.hip (FP8 decode kernels with their split merge,
+csrc/split_merge.h, + launchers),
 csrc/mla_decode_bf16.hip (unquantized-cache decode kernel), csrc/kv_append.hip
 (append-and-quantise kernel), csrc/noalloc.hip (the decode entry point with a
 device-resident split scratch) and csrc/api.cpp (C ABI) into
@@ -53,7 +54,9 @@ def build(verbose: bool = False) -> str:
             obj = os.path.join(tmp, src + ".o")
             cmd = [hipcc, *device_flags(), "-x", lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if lang == "c++":
-                cmd = [hipcc, "-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
+                # host-only source (HIP runtime calls, no kernels): hipcc still
+                # treats it as HIP, so name the one target to skip its default
+                cmd = [hipcc, f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
                        "-c", os.path.join(CSRC, src), "-o", obj]
             _run(cmd, verbose)
             objs.append(obj)

@@ -21,12 +21,13 @@
 //     O accumulators for the value waves;
 //   * the softmax is online, base 2, in fp32, with lazy rescaling;
 //   * a workgroup either writes final bf16 rows or, when a request's keys are
-//     split across workgroups, an fp32 partial (O / l, log2-sum-exp) that
-//     mla_combine merges.
+//     split across workgroups, an fp32 partial (O / l, log2-sum-exp) that the
+//     merge workgroups of the same launch combine (split_merge.h).
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
 #include "mla_internal.h"
+#include "split_merge.h"
 #include "unit_order.h"
 
 namespace mla {
@@ -119,12 +120,6 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Scheduling fence: keeps the compiler from hoisting loads of a later phase into
 // an earlier one (which would raise peak register pressure past the budget).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-
-// 16-byte store with the non-temporal hint (data written once and read once
-// later by another kernel).
-__device__ __forceinline__ void store_nt(float* dst, f32x4 v) {
-  __builtin_nontemporal_store(v, (f32x4*)dst);
-}
 
 // True in every lane when the predicate holds in any lane (wave-uniform result).
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
@@ -233,6 +228,8 @@ struct Layout {
 static_assert(Layout<1>::kTotal <= 160 * 1024 && Layout<9>::kTotal <= 160 * 1024, "LDS budget");
 static_assert(4 * kEpSlice * 4 <= 6 * kTileBytes, "epilogue transposes fit in the tile buffers");
 static_assert(2 * 2 * 18 * 64 * 16 <= 4 * kTileBytes, "q staging fits in the tile buffers of steps 1 and 2");
+static_assert(split_merge::lds_bytes(kThreads / 64) <= Layout<1>::kTotal &&
+              split_merge::lds_bytes(kThreads / 64) <= Layout<9>::kTotal, "merge state fits in the LDS");
 
 // kRecord: also write the block offsets this kernel computes to a.dbg_offsets
 // (the debug entry point's instantiation; the production one carries no such
@@ -251,6 +248,12 @@ mla_decode_kernel(DecodeArgs a) {
   const int sub = wave & 3;
   const int g = lane >> 5;          // lane half
   const int n = lane & 31;          // MFMA column / row within the half
+
+  // ---- Merge workgroups (past the decode grid) combine the split partials.
+  if ((int)blockIdx.x >= a.dgrid) {
+    split_merge::merge_workgroup<kThreads / 64>(a, (int)blockIdx.x - a.dgrid, (LDS_AS float*)lds);
+    return;
+  }
 
   // ---- The work unit (request, row-group pair, key split) of this
   // workgroup: request order, or largest key ranges first (unit_order.h).
@@ -910,142 +913,23 @@ mla_decode_kernel(DecodeArgs a) {
     } else {
       const size_t pidx = ((size_t)b * a.row_groups + rg) * a.num_splits + split;
       float* po = a.ws_o + pidx * kRows * kVDim + 128 * vq4;
-      // 4 columns (16 bytes) per lane, 2 rows per pass; non-temporal stores:
-      // the partials are read once, by the combine
+      // 4 columns (16 bytes) per lane, 2 rows per pass; device-scope stores
+      // that the merge workgroups read (split_merge.h)
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int rl = 2 * k + g;
-        store_nt(po + rl * kVDim + 4 * n, *(LDS_AS const f32x4*)(ep + rl * kEpStride + 4 * n));
+        split_merge::store_dev(po, 4 * (rl * kVDim + 4 * n), *(LDS_AS const f32x4*)(ep + rl * kEpStride + 4 * n));
       }
       if (vq4 == 0 && g == 0) {
         // the row's log2-sum-exp: c2 mO + log2(L)
         const float m0 = st[n], m1 = st[kRows + n], mo = mol[n];
         const float Lt = (m0 == kNegInf ? 0.0f : exp2_fast((m0 - mo) * c2) * st[2 * kRows + n]) +
                          (m1 == kNegInf ? 0.0f : exp2_fast((m1 - mo) * c2) * st[3 * kRows + n]);
-        a.ws_lse[pidx * kRows + n] = Lt > 0.0f ? mo * c2 + __log2f(Lt) : kNegInf;
+        split_merge::store_dev(a.ws_lse + pidx * kRows, 4 * n, Lt > 0.0f ? mo * c2 + __log2f(Lt) : kNegInf);
       }
     }
   }
-}
-
-// ---------------------------------------------------------------- split combine
-// out = sum_s 2^(lse_s - lse) O_s with lse = log2 sum_s 2^lse_s, per row.
-// A workgroup (4 waves) covers (request, row group, a slice of its rows,
-// 64 columns).  In a wave, lane (r, c) owns row r of 8 and columns
-// [4c, 4c + 4) and [32 + 4c, 36 + 4c): every load of the wave reads 8 rows x
-// 128 contiguous bytes.
-// With SP split groups (SP = 1, 2 or 4, from the split count) the waves of a
-// workgroup split the splits: wave w merges every SP-th batch of eight splits
-// (group w % SP) for row block w / SP, and the groups' running states meet
-// through LDS.  A long request with many splits thus spreads over several
-// workgroups and short per-lane chains.
-constexpr int kCombineThreads = 256;
-
-// Split groups: about two batches of eight splits per wave, at most four groups.
-int combine_split_groups(int num_splits) {
-  int sp = 1;
-  while (sp < 4 && 16 * sp < num_splits) sp *= 2;
-  return sp;
-}
-
-__global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(DecodeArgs a, int sp) {
-  __shared__ float st[4][10][64];                   // [wave][M, W, acc[8]][lane]
-  const int chunk = blockIdx.x & 7;                 // 64-column chunk
-  const int rsub = (blockIdx.x >> 3) % sp;          // row slice (32 / sp rows)
-  const int brg = (blockIdx.x >> 3) / sp;
-  const int b = brg / a.row_groups;
-  const int rg = brg % a.row_groups;
-  const int L = (int)min(((const CONST_AS uint32_t*)a.cache_lengths)[b],
-                         (uint32_t)a.max_pages * (uint32_t)a.page_size);
-  const int T = a.tokens_per_split;
-  const int nsplit_eff = L <= 0 ? 1 : (L + T - 1) / T;
-  if (nsplit_eff <= 1) return;                      // (the whole workgroup)
-  const int rows_total = a.q_len * a.num_heads;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int sg = wave % sp;                         // split group
-  const int rl = rsub * (32 / sp) + 8 * (wave / sp) + (lane >> 3);   // row within the group
-  // 8 columns per lane, in two groups of 4 (columns c, c + 32 of the chunk):
-  // each load of the wave then reads 8 rows x 128 contiguous bytes
-  const int col0 = chunk * 64 + (lane & 7) * 4;
-  const int row = rg * kRows + rl;
-
-  const size_t pbase = ((size_t)b * a.row_groups + rg) * a.num_splits;
-  // Online over batches of eight splits: each batch's sixteen O loads and
-  // eight lse loads are in flight together; the running maximum M moves (and
-  // the sums are rescaled) only when a batch raises it.
-  float M = kNegInf, W = 0.0f;
-  float acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  for (int s0 = 8 * sg; s0 < nsplit_eff; s0 += 8 * sp) {
-    f32x4 v[8][2];
-    float ls[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = min(s0 + u, nsplit_eff - 1);
-      ls[u] = a.ws_lse[(pbase + s) * kRows + rl];
-      const f32x4* src = (const f32x4*)(a.ws_o + ((pbase + s) * kRows + rl) * kVDim + col0);
-      v[u][0] = src[0];
-      v[u][1] = src[8];
-    }
-    float mb = kNegInf;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (s0 + u >= nsplit_eff) ls[u] = kNegInf;     // (a repeated last split)
-      mb = fmaxf(mb, ls[u]);
-    }
-    if (mb > M) {
-      const float r = M == kNegInf ? 0.0f : exp2_fast(M - mb);
-      W *= r;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] *= r;
-      M = mb;
-    }
-    if (M == kNegInf) continue;                      // nothing visible yet
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float w = ls[u] == kNegInf ? 0.0f : exp2_fast(ls[u] - M);
-      W += w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[j] = __builtin_fmaf(w, v[u][0][j], acc[j]);
-        acc[4 + j] = __builtin_fmaf(w, v[u][1][j], acc[4 + j]);
-      }
-    }
-  }
-  if (sp > 1) {
-    // split groups 1.. hand their states to group 0 of the same row block
-    if (sg != 0) {
-      st[wave][0][lane] = M;
-      st[wave][1][lane] = W;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) st[wave][2 + j][lane] = acc[j];
-    }
-    __syncthreads();
-    if (sg != 0) return;
-    for (int k = 1; k < sp; ++k) {
-      const int wo = wave + k;
-      const float Mo = st[wo][0][lane], Wo = st[wo][1][lane];
-      const float Mn = fmaxf(M, Mo);
-      const float r0 = M == kNegInf ? 0.0f : exp2_fast(M - Mn);
-      const float r1 = Mo == kNegInf ? 0.0f : exp2_fast(Mo - Mn);
-      W = W * r0 + Wo * r1;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = acc[j] * r0 + st[wo][2 + j][lane] * r1;
-      M = Mn;
-    }
-  }
-  if (row >= rows_total) return;
-  const float inv = W > 0.0f ? 1.0f / W : 0.0f;
-  uint16_t* orow = a.out + ((size_t)b * rows_total + row) * kVDim + col0;
-  u32x2 lo, hi;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    lo[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
-    hi[j] = (uint32_t)f32_to_bf16_bits(acc[4 + 2 * j] * inv) | ((uint32_t)f32_to_bf16_bits(acc[5 + 2 * j] * inv) << 16);
-  }
-  *(u32x2*)orow = lo;
-  *(u32x2*)(orow + 32) = hi;
+  if (nsplit_eff > 1) split_merge::signal_partials(a, b, rgp, split, sub, lane);   // (each value wave)
 }
 
 // ---------------------------------------------------------------- resolve (debug)
@@ -1073,7 +957,29 @@ __global__ void mla_resolve_kernel(const uint32_t* lt, const uint32_t* slt, cons
 size_t partial_bytes(int64_t batch, int64_t row_groups, int64_t num_splits) {
   if (num_splits <= 1) return 0;
   const size_t units = (size_t)batch * (size_t)row_groups * (size_t)num_splits;
-  return units * kRows * kVDim * sizeof(float) + units * kRows * sizeof(float);
+  return kFlagBytes + units * kRows * kVDim * sizeof(float) + units * kRows * sizeof(float);
+}
+
+// Merge grid: units (request, row group, chunk of wave blocks); a chunk is
+// the most 8-row x 64-column wave blocks per workgroup (a power of two
+// dividing `waves`) that still gives about one merge workgroup per compute
+// unit, the remaining waves of the workgroup splitting the key splits.
+int plan_merge(DecodeArgs& a, int dgrid, int waves) {
+  a.dgrid = dgrid;
+  a.merge_nwb = 1;
+  if (a.num_splits <= 1) return 0;
+  int cus = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0) cus = c;
+  }
+  const int64_t groups = (int64_t)a.batch * a.row_groups;
+  int nwb = waves;
+  while (nwb > 1 && groups * (split_merge::kWaveBlocks / nwb) < cus) nwb >>= 1;
+  a.merge_nwb = nwb;
+  const int64_t units = groups * (split_merge::kWaveBlocks / nwb);
+  return (int)(8 * ((units + 7) / 8));
 }
 
 template <int NG, bool kRecord>
@@ -1086,13 +992,14 @@ static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream, hipEvent_
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int grid = decode_grid(a);
+  DecodeArgs args = a;
+  const int grid = decode_grid(a) + plan_merge(args, decode_grid(a), kThreads / 64);
   if (begin && end) {
     // the events take the kernel's own start / end timestamps
     hipExtLaunchKernelGGL((mla_decode_kernel<NG, kRecord>), dim3(grid), dim3(kThreads), lds_bytes, stream,
-                          begin, end, 0, a);
+                          begin, end, 0, args);
   } else {
-    hipLaunchKernelGGL((mla_decode_kernel<NG, kRecord>), dim3(grid), dim3(kThreads), lds_bytes, stream, a);
+    hipLaunchKernelGGL((mla_decode_kernel<NG, kRecord>), dim3(grid), dim3(kThreads), lds_bytes, stream, args);
   }
   return hipGetLastError();
 }
@@ -1110,15 +1017,7 @@ hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stre
                           : launch_main<9, false>(a, stream, main_begin, main_end);
   if (e != hipSuccess) return e;
   if (main_end && !both && (e = hipEventRecord(main_end, stream)) != hipSuccess) return e;
-  if (a.num_splits > 1) e = launch_combine(a, stream);
   return e;
-}
-
-hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
-  const int sp = combine_split_groups(a.num_splits);
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(a.batch * a.row_groups * 8 * sp), dim3(kCombineThreads), 0, stream,
-                     a, sp);
-  return hipGetLastError();
 }
 
 hipError_t launch_resolve(const uint32_t* lt, const uint32_t* slt, const uint32_t* cache_lengths,

@@ -10,7 +10,8 @@
 // Work decomposition and output format are those of the FP8 decode kernel:
 // a workgroup owns a pair of 32-row groups (64 query rows) of one request and
 // one key range; with several key ranges it writes fp32 partials (O / l and the
-// log2-sum-exp) that mla_combine_kernel merges.
+// log2-sum-exp) that the merge workgroups of the same launch combine
+// (split_merge.h).
 //
 // Workgroup = 4 waves; wave w owns 16 query rows (rows 16 (w % 2) .. + 15 of
 // row group w / 2) against all keys and all 512 value columns, so its softmax
@@ -30,6 +31,7 @@
 #include <hip/hip_ext.h>
 
 #include "mla_internal.h"
+#include "split_merge.h"
 #include "unit_order.h"
 
 namespace mla {
@@ -52,6 +54,7 @@ constexpr int kBufs = 4;                         // LDS ring of tiles
 constexpr int kAhead = kBufs - 1;                // tiles in flight ahead of the one in use
 constexpr int kThreadsU = 256;
 constexpr int kLdsBytes = kBufs * kTileBytesU;   // 147456
+static_assert(split_merge::lds_bytes(kThreadsU / 64) <= kLdsBytes, "merge state fits in the LDS");
 constexpr int kDepthChunks = kHeadDim / 32;      // 18 MFMA k-steps of 32
 constexpr int kVBlocks = kVDim / 16;             // 32 output blocks of 16 columns
 // Lazy reference maximum: the reference moves only when a score passes it by
@@ -121,6 +124,12 @@ mla_decode_bf16_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gq = lane >> 4;           // 16-lane group
   const int n = lane & 15;
+
+  // ---- merge workgroups (past the decode grid) combine the split partials
+  if ((int)blockIdx.x >= a.dgrid) {
+    split_merge::merge_workgroup<kThreadsU / 64>(a, (int)blockIdx.x - a.dgrid, (LDS_AS float*)lds);
+    return;
+  }
 
   // ---- unit: (request, row-group pair, key split), in the FP8 kernel's order
   const int rgp_count = (a.row_groups + 1) >> 1;
@@ -329,8 +338,9 @@ mla_decode_bf16_kernel(DecodeArgs a) {
   // ---- epilogue: lane (n, gq) holds O[row n][16 nb + 4 gq + r] in o[nb][r]
   const float l_row = quad_sum(l_part);
   const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-  if (!row_ok) return;
-  if (nsplit_eff == 1) {
+  if (!row_ok) {
+    // no row here; the wave still counts in below
+  } else if (nsplit_eff == 1) {
     uint16_t* orow = a.out + ((size_t)b * rows_total + my_row) * kVDim + 4 * gq;
 #pragma unroll
     for (int nb = 0; nb < kVBlocks; ++nb) {
@@ -340,12 +350,17 @@ mla_decode_bf16_kernel(DecodeArgs a) {
       *(u32x2*)(orow + 16 * nb) = packed;
     }
   } else {
+    // device-scope stores that the merge workgroups read (split_merge.h)
     const size_t pidx = ((size_t)b * a.row_groups + rg) * a.num_splits + split;
-    float* po = a.ws_o + (pidx * kRows + row_in_rg) * kVDim + 4 * gq;
+    float* const po = a.ws_o + pidx * kRows * kVDim;
+    const uint32_t off = 4 * (row_in_rg * kVDim + 4 * gq);
 #pragma unroll
-    for (int nb = 0; nb < kVBlocks; ++nb) *(f32x4*)(po + 16 * nb) = o[nb] * inv;
-    if (gq == 0) a.ws_lse[pidx * kRows + row_in_rg] = l_row > 0.0f ? m_ref * c2 + __log2f(l_row) : kNegInf;
+    for (int nb = 0; nb < kVBlocks; ++nb) split_merge::store_dev(po, off + 64 * nb, o[nb] * inv);
+    if (gq == 0)
+      split_merge::store_dev(a.ws_lse + pidx * kRows, 4 * row_in_rg,
+                             l_row > 0.0f ? m_ref * c2 + __log2f(l_row) : kNegInf);
   }
+  if (nsplit_eff > 1) split_merge::signal_partials(a, b, rgp, split, wave, lane);   // (each of the four waves)
 }
 
 }  // namespace bf16_path
@@ -363,17 +378,18 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, hipEvent_
   hipError_t e;
   const bool both = main_begin && main_end;
   if (main_begin && !both && (e = hipEventRecord(main_begin, stream)) != hipSuccess) return e;
-  const int grid = decode_grid(a);
+  DecodeArgs args = a;
+  const int grid = decode_grid(a) + plan_merge(args, decode_grid(a), bf16_path::kThreadsU / 64);
   if (both) {
     hipExtLaunchKernelGGL(bf16_path::mla_decode_bf16_kernel, dim3(grid), dim3(bf16_path::kThreadsU),
-                          bf16_path::kLdsBytes, stream, main_begin, main_end, 0, a);
+                          bf16_path::kLdsBytes, stream, main_begin, main_end, 0, args);
   } else {
     hipLaunchKernelGGL(bf16_path::mla_decode_bf16_kernel, dim3(grid), dim3(bf16_path::kThreadsU),
-                       bf16_path::kLdsBytes, stream, a);
+                       bf16_path::kLdsBytes, stream, args);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (main_end && !both && (e = hipEventRecord(main_end, stream)) != hipSuccess) return e;
-  return a.num_splits > 1 ? launch_combine(a, stream) : hipSuccess;
+  return hipSuccess;
 }
 
 }  // namespace mla

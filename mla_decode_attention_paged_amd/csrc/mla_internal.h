@@ -37,6 +37,7 @@ struct DecodeArgs {
   uint16_t* out;                     // bf16 bits [B, Q, H, 512]
   float* ws_o;                       // split partials O   [B, RG, S, 32, 512] (fp32)
   float* ws_lse;                     // split partials lse [B, RG, S, 32]      (log2 domain)
+  uint32_t* ws_flags;                // split completion words (kFlagBytes; split_merge.h)
   int64_t page_stride;               // bytes between pages of blocks (kv_dim*num_layers*P*576)
   int64_t layer_offset;              // bytes to (kv 0, layer_idx, slot 0) inside a page
   int64_t spage_stride;              // floats between pages of scales
@@ -45,6 +46,8 @@ struct DecodeArgs {
   int32_t row_groups, num_splits, tokens_per_split;
   int32_t grid_units;                // batch * row_groups * num_splits
   int32_t lpt;                       // 1: largest (request, split) key ranges first
+  int32_t dgrid;                     // decode workgroups; the merge workgroups follow them
+  int32_t merge_nwb;                 // 8-row x 64-column wave blocks per merge workgroup
   float sm_log2;                     // softmax_scale * log2(e)
   // Debug record of the decode kernel's own page resolution (null in normal
   // calls): for 16-key block k of request b, [b, k, 0] = byte offset of the
@@ -55,6 +58,17 @@ struct DecodeArgs {
   int32_t dbg_blocks;
 };
 
+// Workspace of a split plan: the completion counters (kFlagBytes, at the
+// start, the same place for every plan, so that a workspace reused across
+// shapes never finds partial data where counters go), then the partial O,
+// then the partial lse.  0 when num_splits <= 1.  Split plans are limited to
+// kSplitFlagPairs (request, row-group pair) units.
+constexpr int64_t kSplitFlagPairs = 8192;
+// ... and kSplitFlagEntries (request, row-group pair, split) units, with at
+// most kMaxSplits splits per request.
+constexpr int64_t kSplitFlagEntries = 65536;
+constexpr int64_t kMaxSplits = 4096;
+constexpr size_t kFlagBytes = (size_t)(kSplitFlagPairs + kSplitFlagEntries) * sizeof(uint32_t);   // 288 KiB
 size_t partial_bytes(int64_t batch, int64_t row_groups, int64_t num_splits);
 
 // Arguments of the append-and-quantise kernel (kv_append.hip).
@@ -73,20 +87,20 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs& a, int scale_groups, hipStream_t stream);
 
-// Launch the decode kernel (and the split combine when num_splits > 1).  The
-// optional events are recorded right before / after the decode kernel.
+// Launch the decode kernel (with its split merge when num_splits > 1).  The
+// optional events are recorded right before / after the launch.
 hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stream,
                          hipEvent_t main_begin = nullptr, hipEvent_t main_end = nullptr);
 
-// Launch the unquantized (bf16 cache) decode kernel, then the split combine
-// when num_splits > 1.  DecodeArgs as for the FP8 kernel with blocks holding
+// Launch the unquantized (bf16 cache) decode kernel (with its split merge
+// when num_splits > 1).  DecodeArgs as for the FP8 kernel with blocks holding
 // bf16 rows (page_stride / layer_offset in bytes); scales and slt are unused.
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin = nullptr,
                               hipEvent_t main_end = nullptr);
 
-// The split combine alone (mla_decode.hip): merges the fp32 partials in a.ws_o /
-// a.ws_lse into a.out.
-hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
+// Merge workgroups to append to a decode grid of `waves`-wave workgroups:
+// sets a.dgrid and a.merge_ncb and returns the merge grid (0 when unsplit).
+int plan_merge(DecodeArgs& a, int dgrid, int waves);
 
 // The decode with a caller-given workspace (api.cpp), for other entry points.
 mla_status decode_with_workspace(const void* q, const void* blocks, const float* scales,

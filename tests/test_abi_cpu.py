@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert binding.mla_abi_version() == 4
+    assert binding.mla_abi_version() == 5
     for code in range(7):
         assert lib.mla_status_string(code).decode()
     assert lib.mla_status_string(99).decode() == "unknown status"
@@ -118,12 +118,26 @@ def test_plan_covers_the_key_range(lib):
             assert p.workspace_bytes == 0
         else:
             units = B * p.row_groups * p.num_splits
-            assert p.workspace_bytes == units * 32 * 512 * 4 + units * 32 * 4
+            # 288 KiB of split completion flags, then O and lse partials
+            assert p.workspace_bytes == 294912 + units * 32 * 512 * 4 + units * 32 * 4
 
 
 def test_plan_explicit_splits_clamped(lib):
     st, p = plan(lib, good_shape(max_pages=2, page_size=64), splits=50)   # 128 keys -> 1 chunk
     assert st == OK and p.num_splits == 1
+
+
+def test_split_plans_limited_to_the_merge_counters(lib):
+    # 8192 (request, row-group pair) units have completion counters; more
+    # units run unsplit (automatic plan) or are refused (explicit count)
+    shape = good_shape(batch=8193, num_q_heads=64, max_pages=256, page_size=64, num_blocks=64)
+    st, p = plan(lib, shape)
+    assert st == OK and p.num_splits == 1 and p.workspace_bytes == 0
+    st, p = plan(lib, shape, splits=2)
+    assert st == UNSUP
+    shape = good_shape(batch=8192, num_q_heads=64, max_pages=256, page_size=64, num_blocks=64)
+    st, p = plan(lib, shape, splits=2)
+    assert st == OK and p.num_splits == 2
 
 
 def test_resolve_rejects_bad_args(lib):

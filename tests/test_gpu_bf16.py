@@ -5,7 +5,7 @@ The gate is the one of the FP8 path: e = |gpu - bf16(oracle)| / max(1, |oracle|)
 max e <= 1e-2 and mean e <= 1e-3.  Cases cover NaN-poisoned unused slots,
 pages and layers, ragged tails around the 32-key tile and 16-key load block,
 lengths below q_len, empty requests, forced split counts (partials merged by
-the combine kernel), causal q_len > 1, odd head counts, and the full-size
+the split merge of the same launch), causal q_len > 1, odd head counts, and the full-size
 uniform workload (16 x 4096 keys, 128 heads) on sampled requests in the
 launch configuration the benchmark times.
 """
@@ -86,7 +86,7 @@ def test_uniform_full_size_sampled(gpu_device):
 
 
 def test_long_context_sampled(gpu_device):
-    """One request of 131072 keys (page 128): many splits merged by the combine kernel."""
+    """One request of 131072 keys (page 128): many splits merged by the split merge."""
     say("bf16 long 131072")
     w = _w(gpu_device, 1, 128, [131072], 128, 576, seed=3001, poison=False)
     check_gate(run_bf16(w), oracle_decode_unquantized(w.to("cpu")), "bf16 long")
@@ -101,7 +101,7 @@ def test_q4_rows_equal_q1_calls(gpu_device):
 
 def test_split_partials_beyond_f16_range(gpu_device):
     """Cache rows x 2^14 and q x 2^-14: the same scores, O x 2^14, past f16's
-    largest finite value; the fp32 split partials and the combine must carry
+    largest finite value; the fp32 split partials and the split merge must carry
     such outputs, and P (bf16 hi + lo) must stay exact enough at that scale."""
     say("bf16 cache, partials beyond the f16 range")
     w = _w(gpu_device, 2, 128, [3000, 700], 64, 576, seed=74, poison=True, kv_dtype="bf16")

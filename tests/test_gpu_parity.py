@@ -228,7 +228,7 @@ def test_split_partials_beyond_f16_range(gpu_device, gran, e):
     """Large scales: scales x 2^e and q x 2^-e leave every score unchanged and
     multiply O by 2^e exactly (powers of two).  With per-token scales (e = 14)
     the outputs pass f16's largest finite value (65504): the fp32 split
-    partials and the combine must carry them, and the per-tile threshold
+    partials and the split merge must carry them, and the per-tile threshold
     must keep P' = p * s finite in f16.  With group scales (e = 11) the scales
     reach the range where P' = p * s_g depends on the threshold's bound
     p <= 2^8 (the documented contract is s_g <= 255)."""
@@ -249,7 +249,7 @@ def test_split_partials_beyond_f16_range(gpu_device, gran, e):
 
 @pytest.mark.parametrize("splits", [24, 40, 157])
 def test_many_splits_ragged(gpu_device, splits):
-    """Many key splits (the combine then merges in several lane groups per row)
+    """Many key splits (the merge workgroups then fold them in several waves per wave block)
     with requests that use fewer splits than the plan, or none."""
     say("many splits", splits)
     w = _w(gpu_device, 3, 128, [20000, 3000, 5], 128, 576, seed=75, poison=True)
