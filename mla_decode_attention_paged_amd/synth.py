@@ -190,6 +190,51 @@ def make_workload(batch, num_heads, cache_lengths, page_size, granularity, *, q_
         page_size=P, granularity=int(granularity), name=name)
 
 
+@dataclasses.dataclass
+class RaggedWorkload(Workload):
+    """A decode call whose requests have their own query counts: q is packed
+    [T, H, 576], request b owning rows q_offsets[b] .. q_offsets[b + 1] - 1;
+    q_len holds the largest count (the batch's max_prompt_length)."""
+
+    q_offsets: torch.Tensor | None = None   # int32 [B + 1], from 0 to T
+
+    @property
+    def batch(self) -> int:
+        return self.q_offsets.shape[0] - 1
+
+    @property
+    def num_heads(self) -> int:
+        return self.q.shape[1]
+
+    def q_counts(self) -> list[int]:
+        o = [int(v) for v in self.q_offsets.cpu().tolist()]
+        return [o[b + 1] - o[b] for b in range(len(o) - 1)]
+
+    def to(self, device) -> "RaggedWorkload":
+        w = Workload.to(self, device)
+        return dataclasses.replace(w, q_offsets=self.q_offsets.to(device))
+
+
+def make_ragged_workload(q_counts, num_heads, cache_lengths, page_size, granularity, *, seed=0,
+                         device="cpu", **kw):
+    """The cache of make_workload (same recipe and keyword arguments) with
+    per-request query counts q_counts (each >= 0, normally <= the request's
+    cache length): q ~ bf16(N(0, 1)) packed [sum(q_counts), H, 576]."""
+    counts = [int(c) for c in q_counts]
+    if any(c < 0 for c in counts):
+        raise ValueError("query counts are >= 0")
+    w = make_workload(len(counts), num_heads, cache_lengths, page_size, granularity, q_len=1,
+                      seed=seed, device=device, **kw)
+    dgen = torch.Generator(device=device)
+    dgen.manual_seed(int(seed) + 104729)
+    q = torch.randn((sum(counts), num_heads, HEAD_DIM), generator=dgen, device=device,
+                    dtype=torch.float32).to(torch.bfloat16)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=device)
+    fields = {f.name: getattr(w, f.name) for f in dataclasses.fields(Workload)}
+    fields.update(q=q, q_len=max(1, max(counts)))
+    return RaggedWorkload(**fields, q_offsets=offs)
+
+
 def _u32_view(t: torch.Tensor) -> torch.Tensor:
     """int64 ids in [0, 2^32) stored as int32 tensors holding the same 32 bits."""
     t = t.to(torch.int64)

@@ -12,6 +12,7 @@ from .mla_oracle import (  # noqa: F401
     attention_rows,
     bf16_round,
     decode,
+    decode_ragged,
     decode_range,
     e4m3fn_value,
     gather_dequant,

@@ -40,6 +40,14 @@ Readings taken where the pages are silent (each listed in the design doc):
   R7  V_j = K_j[:dv] with the same scales (dv = 512 for the MLA workloads).
   R8  softmax_scale multiplies the full-depth dot product; q already carries rope.
   R9  rows with no visible key give O = 0 and lse = -inf.
+  R16 per-request query counts ("generic_get_paged_cache_with_scales", Args:
+      ``max_prompt_length`` is the largest query length of the batch, so the
+      requests' own lengths may differ; "KVCacheScalesMHAOperand",
+      ``create_ragged_tma_tile``: ragged rows): the queries of all requests are
+      packed request after request along the first axis, request b owning
+      rows [q_offsets[b], q_offsets[b + 1]) of an offsets array of batch + 1
+      non-decreasing entries starting at 0; its count n_b may be 0 (no rows)
+      and R1 applies to it with q_len = n_b.
 
 Everything is evaluated in float64 with no blocking, fusion or reordering: the
 gather is a per-token integer loop over the page table, and the contractions are
@@ -61,6 +69,7 @@ __all__ = [
     "attention_rows",
     "decode",
     "decode_range",
+    "decode_ragged",
     "merge_partials",
 ]
 
@@ -238,6 +247,48 @@ def decode(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths,
             o, l, _ = attention_rows(q[b, i], K, n_vis, softmax_scale, dv)
             O[b, i] = o
             lse[b, i] = l
+    return (O, lse) if return_lse else O
+
+
+def decode_ragged(q, q_offsets, blocks, scales, lookup_table, scales_lookup_table, cache_lengths,
+                  layer_idx, softmax_scale, dv=512, requests=None, return_lse=False):
+    """MLA decode with per-request query counts (reading R16): O[t, h, :dv].
+
+    q: float [T, H, head_dim], the queries of request b in rows
+    q_offsets[b] .. q_offsets[b + 1] - 1 (T = q_offsets[-1]); the other
+    arguments as for ``decode``.  Query i (0-based) of request b sees keys
+    j <= L_b - n_b + i with n_b = q_offsets[b + 1] - q_offsets[b] (reading
+    R1 per request).  ``requests`` restricts the work to a subset (other rows
+    are left as NaN).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    offs = [int(x) for x in np.asarray(q_offsets).reshape(-1)]
+    B = len(offs) - 1
+    T, H, D = q.shape
+    if B < 1 or offs[0] != 0 or offs[-1] != T or any(offs[b + 1] < offs[b] for b in range(B)):
+        raise ValueError("q_offsets must be batch + 1 non-decreasing entries from 0 to q.shape[0]")
+    if blocks.ndim != 6 or scales.ndim != 6 or blocks.shape[-1] != D or blocks.shape[4] != 1:
+        raise ValueError("blocks / scales shapes do not match q")
+    if not (0 <= layer_idx < blocks.shape[2]):
+        raise ValueError("layer_idx out of range")
+    P = blocks.shape[3]
+    G = D // scales.shape[-1]
+    lt = np.asarray(lookup_table)
+    slt = None if scales_lookup_table is None else np.asarray(scales_lookup_table)
+    O = np.full((T, H, dv), np.nan)
+    lse = np.full((T, H), np.nan)
+    for b in (range(B) if requests is None else requests):
+        first, n = offs[b], offs[b + 1] - offs[b]
+        if n == 0:
+            continue
+        L = int(cache_lengths[b])
+        rows = resolve(lt[b:b + 1], None if slt is None else slt[b:b + 1], [L], P)[0]
+        K = gather_dequant(blocks, scales, rows, layer_idx, G)
+        for i in range(n):
+            n_vis = max(0, min(L, L - n + i + 1))        # readings R1, R16
+            o, l, _ = attention_rows(q[first + i], K, n_vis, softmax_scale, dv)
+            O[first + i] = o
+            lse[first + i] = l
     return (O, lse) if return_lse else O
 
 

@@ -26,6 +26,14 @@ def oracle_decode(w, batches=None, return_lse=False):
                   batches=batches, return_lse=return_lse)
 
 
+def oracle_decode_ragged(w, requests=None, return_lse=False):
+    from oracle import decode_ragged
+    q, blocks, scales, lt, slt, cl = to_numpy(w)
+    offs = w.q_offsets.cpu().numpy().astype(np.int64)
+    return decode_ragged(q, offs, blocks, scales, lt, slt, cl, w.layer_idx, w.softmax_scale,
+                         requests=requests, return_lse=return_lse)
+
+
 def oracle_decode_unquantized(w, batches=None, return_lse=False):
     from oracle import decode_unquantized
     q, blocks, _, lt, _, cl = to_numpy(w)

@@ -11,7 +11,8 @@ torch's bfloat16 cast; the hand-worked resolution and two-key examples
 (tests/golden/); identity paging against torch's scaled_dot_product_attention;
 rows summing to 1; one cached key returning its value row; the causal rule;
 equal group scales against per-token scales; page permutation invariance; the
-log-sum-exp merge; and a scalar brute force with math.fsum.
+log-sum-exp merge; a scalar brute force with math.fsum; and the same brute
+force over per-request query counts.
 """
 
 import json
@@ -235,8 +236,38 @@ def pin_brute(o):
                     assert abs(O[b, i, h, c] - ref) <= 1e-12 * max(1.0, abs(ref))
 
 
+def pin_ragged(o):
+    """Per-request query counts (3, 0, 2, 1): scalar loops and math.fsum, each
+    request causal among its own new tokens."""
+    lengths, counts = [6, 4, 9, 3], [3, 0, 2, 1]
+    P, G, H, sm = 16, 64, 2, 0.09
+    _, blocks, scales, lt, slt = _random_cache(13, lengths, P=P, G=G, indep=True, H=H)
+    rng = np.random.default_rng(14)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    q = rng.standard_normal((int(offs[-1]), H, 576))
+    O = o.decode_ragged(q, offs, blocks, scales, lt, slt, lengths, 0, sm)
+    for b, L in enumerate(lengths):
+        K = []
+        for t in range(L):
+            page, slot, spage = int(lt[b, t // P]), t % P, int(slt[b, t // P])
+            K.append([_closed_form_e4m3(blocks[page, 0, 0, slot, 0, d]) *
+                      float(scales[spage, 0, 0, slot, 0, d // G]) for d in range(576)])
+        n = counts[b]
+        for i in range(n):
+            vis = L - n + i + 1
+            for h in range(H):
+                row = int(offs[b]) + i
+                s = [sm * math.fsum(q[row, h, d] * K[j][d] for d in range(576)) for j in range(vis)]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                den = math.fsum(e)
+                for c in (0, 300, 511):
+                    ref = math.fsum(e[j] / den * K[j][c] for j in range(vis))
+                    assert abs(O[row, h, c] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
 PINS = [pin_codec, pin_bf16, pin_resolve_golden, pin_two_keys, pin_dense, pin_rows_sum, pin_one_key,
-        pin_causal, pin_group_equal, pin_perm, pin_merge, pin_brute]
+        pin_causal, pin_group_equal, pin_perm, pin_merge, pin_brute, pin_ragged]
 
 MUTANTS = {
     "softmax scale dropped": ("scores = softmax_scale * (q_rows @ Kv.T)", "scores = (q_rows @ Kv.T)"),
@@ -263,6 +294,13 @@ MUTANTS = {
         "coef = np.where(finite, 1.0, 0.0) * np.exp(lses - np.where(finite, Msafe, 0.0))"),
     "range causal limit off by one": ("hi = min(t1, max(0, min(L, L - Q + i + 1)))",
                                       "hi = min(t1, max(0, min(L, L - Q + i + 2)))"),
+    "ragged causal limit from the largest count": (
+        "n_vis = max(0, min(L, L - n + i + 1))        # readings R1, R16",
+        "n_vis = max(0, min(L, L - max(offs[k + 1] - offs[k] for k in range(B)) + i + 1))"),
+    "ragged query rows shifted by one": ("o, l, _ = attention_rows(q[first + i], K, n_vis, softmax_scale, dv)",
+                                         "o, l, _ = attention_rows(q[min(first + i + 1, T - 1)], K, n_vis, softmax_scale, dv)"),
+    "ragged count from the wrong offsets": ("first, n = offs[b], offs[b + 1] - offs[b]",
+                                            "first, n = offs[b], offs[b + 1] - offs[max(b - 1, 0)]"),
 }
 
 
