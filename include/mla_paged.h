@@ -191,6 +191,36 @@ mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, cons
                                          hipStream_t stream);
 
 /*
+ * mla_decode_paged_fp8_ragged — mla_decode_paged_fp8_splits for requests with
+ * their own query counts ("generic_get_paged_cache_with_scales" page, Args:
+ * max_prompt_length is the batch's largest query length; "KVCacheScalesMHA-
+ * Operand" page, create_ragged_tma_tile: ragged query rows).  The queries are
+ * packed request after request:
+ *   q          bf16 [T, num_q_heads, 576], T = q_offsets[batch]
+ *   q_offsets  device uint32 [batch + 1], q_offsets[0] = 0, non-decreasing:
+ *              request b owns q rows q_offsets[b] .. q_offsets[b + 1] - 1, its
+ *              n_b = q_offsets[b + 1] - q_offsets[b] new tokens (0 allowed: no
+ *              output rows; n_b <= max_q_len)
+ *   max_q_len  the largest n_b (the plan is sized for it, as for q_len)
+ *   out        bf16 [T, num_q_heads, 512] (written for every packed row)
+ * Query i of request b sees keys j <= cache_lengths[b] - n_b + i (each request
+ * causal among its own new tokens).  The other arguments, the plan
+ * (mla_decode_paged_fp8_plan with q_len = max_q_len), the workspace, split
+ * counts and errors are those of mla_decode_paged_fp8_splits; MLA_ERR_NULL
+ * when q_offsets is NULL, MLA_ERR_UNSUPPORTED when it is not 4-byte aligned.
+ * The offsets are read on the device only: offsets that break the contract
+ * above give undefined results.
+ */
+mla_status mla_decode_paged_fp8_ragged(const void* q, const uint32_t* q_offsets, const void* blocks,
+                                       const float* scales, const uint32_t* lookup_table,
+                                       const uint32_t* scales_lookup_table, /* nullable */
+                                       const uint32_t* cache_lengths, int32_t layer_idx,
+                                       int32_t max_q_len, float softmax_scale, void* out,
+                                       const mla_shape* shape, void* workspace,
+                                       size_t workspace_bytes, int32_t num_splits,
+                                       hipStream_t stream);
+
+/*
  * mla_decode_paged_fp8_block_offsets — debug variant of
  * mla_decode_paged_fp8_splits that also reports the page resolution the
  * decode kernel itself computed for its loads ("generic_get_paged_cache_with_

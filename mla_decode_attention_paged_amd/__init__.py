@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     mla_decode_paged_fp8,
     mla_decode_paged_fp8_noalloc,
     mla_decode_paged_fp8_plan,
+    mla_decode_paged_fp8_ragged,
     mla_resolve_pages,
     new_workspace,
     workspace_bytes,

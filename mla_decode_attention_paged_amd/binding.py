@@ -88,6 +88,10 @@ def load_library() -> ctypes.CDLL:
     lib.mla_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.mla_decode_paged_fp8_block_offsets.argtypes = common + [ctypes.c_int32, vp, ctypes.c_int32, vp]
     lib.mla_decode_paged_fp8_block_offsets.restype = ctypes.c_int
+    lib.mla_decode_paged_fp8_ragged.argtypes = [vp, u32p, vp, f32p, u32p, u32p, u32p, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_float, vp, ctypes.POINTER(MlaShape), vp,
+                                                ctypes.c_size_t, ctypes.c_int32, vp]
+    lib.mla_decode_paged_fp8_ragged.restype = ctypes.c_int
     bf16_common = [vp, vp, u32p, u32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp,
                    ctypes.POINTER(MlaShape), vp, ctypes.c_size_t]
     lib.mla_decode_paged_bf16.argtypes = bf16_common + [vp]
@@ -264,6 +268,70 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
         st = lib.mla_decode_paged_fp8_splits(*args, int(num_splits), _stream_handle(dev))
     if st != MLA_OK:
         raise MlaError(st, "mla_decode_paged_fp8")
+    return out
+
+
+def mla_decode_paged_fp8_ragged(q, q_offsets, blocks, scales, lookup_table, scales_lookup_table,
+                                cache_lengths, layer_idx, softmax_scale, max_q_len=None, out=None,
+                                workspace=None, num_splits=None):
+    """Decode with per-request query counts; returns `out` (bf16 [T, H, 512]).
+
+    q bf16 [T, H, 576] packed request after request; q_offsets int32 [B + 1]
+    on the device (request b owns rows q_offsets[b] .. q_offsets[b + 1] - 1);
+    the cache arguments as for mla_decode_paged_fp8.  max_q_len: the largest
+    per-request count; when None the offsets are copied to the host (a
+    synchronisation), checked, and the largest count taken from them.
+    workspace / num_splits as for mla_decode_paged_fp8.
+    """
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("mla_decode_paged_fp8_ragged runs on the GPU only; got tensors on " + str(dev))
+    _check_tensor("q", q, (torch.bfloat16,), 3, dev)
+    _check_tensor("q_offsets", q_offsets, (torch.int32,), 1, dev)
+    _check_tensor("blocks", blocks, (torch.uint8, torch.float8_e4m3fn), 6, dev)
+    _check_tensor("scales", scales, (torch.float32,), 6, dev)
+    _check_tensor("lookup_table", lookup_table, (torch.int32,), 2, dev)
+    if scales_lookup_table is not None:
+        _check_tensor("scales_lookup_table", scales_lookup_table, (torch.int32,), 2, dev)
+    _check_tensor("cache_lengths", cache_lengths, (torch.int32,), 1, dev)
+    T, H, D = q.shape
+    B = lookup_table.shape[0]
+    if q_offsets.shape[0] != B + 1 or cache_lengths.shape[0] != B:
+        raise ValueError("q_offsets must hold batch + 1 entries and cache_lengths batch entries")
+    if blocks.shape[1:5] != scales.shape[1:5]:
+        raise ValueError("scales dims 1..4 must equal blocks dims 1..4")
+    if blocks.shape[5] != D:
+        raise ValueError("head_dim of q and blocks differ")
+    if scales_lookup_table is not None and scales_lookup_table.shape != lookup_table.shape:
+        raise ValueError("scales_lookup_table shape must equal lookup_table shape")
+    if max_q_len is None:
+        offs = q_offsets.cpu().tolist()
+        counts = [offs[b + 1] - offs[b] for b in range(B)]
+        if offs[0] != 0 or offs[-1] != T or min(counts) < 0:
+            raise ValueError("q_offsets must be non-decreasing from 0 to q.shape[0]")
+        max_q_len = max(1, max(counts))
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    _check_tensor("out", out, (torch.bfloat16,), 3, dev)
+    if tuple(out.shape) != (T, H, 512):
+        raise ValueError(f"out must be [T, H, 512], got {tuple(out.shape)}")
+    NB, KVD, NL, P, HKV, _ = blocks.shape
+    shp = MlaShape(batch=B, num_q_heads=H, head_dim=D, v_dim=512, num_blocks=NB, kv_dim=KVD, num_layers=NL,
+                   page_size=P, num_kv_heads=HKV, num_scale_blocks=scales.shape[0],
+                   scale_groups=scales.shape[-1], max_pages=lookup_table.shape[1])
+    want = 0 if num_splits is None else int(num_splits)
+    if workspace is None:
+        need = mla_decode_paged_fp8_plan((B, int(max_q_len), H, D), tuple(blocks.shape), tuple(scales.shape),
+                                         tuple(lookup_table.shape), int(max_q_len), want)["workspace_bytes"]
+        workspace = new_workspace(need, dev) if need > 0 else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.mla_decode_paged_fp8_ragged(_ptr(q), _ptr(q_offsets), _ptr(blocks), _ptr(scales), _ptr(lookup_table),
+                                         _ptr(scales_lookup_table), _ptr(cache_lengths), int(layer_idx),
+                                         int(max_q_len), float(softmax_scale), _ptr(out), ctypes.byref(shp),
+                                         _ptr(workspace), ws_bytes, want, _stream_handle(dev))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_decode_paged_fp8_ragged")
     return out
 
 

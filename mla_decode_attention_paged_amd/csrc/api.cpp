@@ -157,11 +157,13 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
                        size_t workspace_bytes, int32_t num_splits, bool explicit_splits,
                        hipStream_t stream, hipEvent_t main_begin = nullptr,
                        hipEvent_t main_end = nullptr, bool unquantized = false,
-                       uint64_t* dbg_offsets = nullptr, int32_t dbg_blocks = 0) {
+                       uint64_t* dbg_offsets = nullptr, int32_t dbg_blocks = 0,
+                       const uint32_t* q_offsets = nullptr) {
   mla_status st = check_args(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
                              q_len, softmax_scale, out, shape, num_splits, unquantized);
   if (st != MLA_OK) return st;
   if (!aligned(workspace, 16)) return MLA_ERR_UNSUPPORTED;
+  if (q_offsets && !aligned(q_offsets, 4)) return MLA_ERR_UNSUPPORTED;
 
   mla_plan plan;
   if (explicit_splits && num_splits > 0) {
@@ -178,6 +180,7 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
 
   mla::DecodeArgs a{};
   a.q = (const uint16_t*)q;
+  a.q_offsets = q_offsets;
   a.blocks = (const uint8_t*)blocks;
   a.scales = unquantized ? nullptr : scales;
   a.lt = lookup_table;
@@ -297,6 +300,18 @@ mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, cons
   return decode_impl(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
                      q_len, softmax_scale, out, shape, workspace, workspace_bytes, num_splits,
                      num_splits > 0, stream, main_begin, main_end);
+}
+
+mla_status mla_decode_paged_fp8_ragged(const void* q, const uint32_t* q_offsets, const void* blocks,
+                                       const float* scales, const uint32_t* lookup_table,
+                                       const uint32_t* scales_lookup_table, const uint32_t* cache_lengths,
+                                       int32_t layer_idx, int32_t max_q_len, float softmax_scale, void* out,
+                                       const mla_shape* shape, void* workspace, size_t workspace_bytes,
+                                       int32_t num_splits, hipStream_t stream) {
+  if (!q_offsets) return MLA_ERR_NULL;
+  return decode_impl(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
+                     max_q_len, softmax_scale, out, shape, workspace, workspace_bytes, num_splits,
+                     num_splits > 0, stream, nullptr, nullptr, false, nullptr, 0, q_offsets);
 }
 
 mla_status mla_decode_paged_fp8_block_offsets(const void* q, const void* blocks, const float* scales,

@@ -273,11 +273,14 @@ mla_decode_kernel(DecodeArgs a) {
   const int T = a.tokens_per_split;
   const int nsplit_eff = L <= 0 ? 1 : (L + T - 1) / T;
   if (split >= nsplit_eff) return;             // no keys here; nothing to write
+  const RequestRows rq = request_rows(a, b);
+  const int rows_total = rq.count * a.num_heads;   // this request's query rows (query-major)
+  if (2 * rgp * kRows >= rows_total) return;   // the pair holds none of them (fewer queries than the largest)
+  const size_t row_base = (size_t)rq.first * a.num_heads;
   const int t_lo = split * T;
   const int t_hi = min(L, t_lo + T);
   const int ntiles = (t_hi - t_lo + kTile - 1) / kTile;
   const int nsteps = (ntiles + 1) / 2;
-  const int rows_total = a.q_len * a.num_heads;
   const float c2 = a.sm_log2;                  // scores are kept unscaled; exponents are c2 * (x - m)
 
   // ---- LDS regions
@@ -425,7 +428,7 @@ mla_decode_kernel(DecodeArgs a) {
     const bool row_ok = my_row < rows_total;
     const int my_i = row_ok ? my_row / a.num_heads : 0;
     // keys visible to this row: j < L - Q + i + 1, clipped to this split
-    const int lim = row_ok ? min(L - a.q_len + my_i + 1, t_hi) : t_hi;
+    const int lim = row_ok ? min(L - rq.count + my_i + 1, t_hi) : t_hi;
     int lim_min = row_ok ? lim : 0x7fffffff;
     for (int off = 16; off >= 1; off >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
     lim_min = __builtin_amdgcn_readfirstlane(min(lim_min, __shfl_xor(lim_min, 32)));
@@ -452,7 +455,7 @@ mla_decode_kernel(DecodeArgs a) {
     {
       const int row = (2 * rgp + par) * kRows + n;
       const bool ok = row < rows_total;
-      const uint16_t* qrow = a.q + ((size_t)b * rows_total + (ok ? row : 0)) * kHeadDim + 32 * d + 16 * g;
+      const uint16_t* qrow = a.q + (row_base + (ok ? row : 0)) * kHeadDim + 32 * d + 16 * g;
 #pragma unroll
       for (int s = 0; s < 9; ++s) {
         const u32x4* src = (const u32x4*)(qrow + 64 * s);
@@ -907,7 +910,7 @@ mla_decode_kernel(DecodeArgs a) {
             packed[j] = (uint32_t)f32_to_bf16_bits(v0[2 * j]) | ((uint32_t)f32_to_bf16_bits(v0[2 * j + 1]) << 16);
             packed[2 + j] = (uint32_t)f32_to_bf16_bits(v1[2 * j]) | ((uint32_t)f32_to_bf16_bits(v1[2 * j + 1]) << 16);
           }
-          *(u32x4*)(a.out + ((size_t)b * rows_total + row) * kVDim + 128 * vq4 + c8) = packed;
+          *(u32x4*)(a.out + (row_base + row) * kVDim + 128 * vq4 + c8) = packed;
         }
       }
     } else {

@@ -146,10 +146,13 @@ mla_decode_bf16_kernel(DecodeArgs a) {
   const int T = a.tokens_per_split;
   const int nsplit_eff = L <= 0 ? 1 : (L + T - 1) / T;
   if (split >= nsplit_eff) return;
+  const RequestRows rq = request_rows(a, b);
+  const int rows_total = rq.count * a.num_heads;   // this request's query rows (query-major)
+  if (2 * rgp * kRows >= rows_total) return;   // the pair holds none of them
+  const size_t row_base = (size_t)rq.first * a.num_heads;
   const int t_lo = split * T;
   const int t_hi = min(L, t_lo + T);
   const int ntiles = (t_hi - t_lo + 31) / 32;
-  const int rows_total = a.q_len * a.num_heads;
   const float c2 = a.sm_log2;
 
   // ---- this lane's query row (row n of the wave's 16)
@@ -159,12 +162,12 @@ mla_decode_bf16_kernel(DecodeArgs a) {
   const bool row_ok = rg < a.row_groups && my_row < rows_total;
   const int my_i = row_ok ? my_row / a.num_heads : 0;
   // keys visible to this row: j < L - Q + i + 1, clipped to the split
-  const int lim = row_ok ? min(L - a.q_len + my_i + 1, t_hi) : t_hi;
+  const int lim = row_ok ? min(L - rq.count + my_i + 1, t_hi) : t_hi;
 
   // q as the B operand of S^T = K Q^T: lane (n, gq) holds depth 32 kc + 8 gq .. + 7 of its row
   bf16x8 qf[kDepthChunks];
   {
-    const uint16_t* qrow = a.q + ((size_t)b * rows_total + (row_ok ? my_row : 0)) * kHeadDim + 8 * gq;
+    const uint16_t* qrow = a.q + (row_base + (row_ok ? my_row : 0)) * kHeadDim + 8 * gq;
 #pragma unroll
     for (int kc = 0; kc < kDepthChunks; ++kc) {
       const u32x4 v = row_ok ? *(const u32x4*)(qrow + 32 * kc) : u32x4{0, 0, 0, 0};
@@ -341,7 +344,7 @@ mla_decode_bf16_kernel(DecodeArgs a) {
   if (!row_ok) {
     // no row here; the wave still counts in below
   } else if (nsplit_eff == 1) {
-    uint16_t* orow = a.out + ((size_t)b * rows_total + my_row) * kVDim + 4 * gq;
+    uint16_t* orow = a.out + (row_base + my_row) * kVDim + 4 * gq;
 #pragma unroll
     for (int nb = 0; nb < kVBlocks; ++nb) {
       u32x2 packed;

@@ -28,13 +28,14 @@ constexpr int kMinWaveSplitKeys = 2048;
 // Everything the main kernel needs, by value.  Offsets are precomputed on the
 // host from the contiguous row-major shapes of the blocks / scales tensors.
 struct DecodeArgs {
-  const uint16_t* q;                 // bf16 bits [B, Q, H, 576]
+  const uint16_t* q;                 // bf16 bits [B, Q, H, 576], or [T, H, 576] with q_offsets
+  const uint32_t* q_offsets;         // [B + 1] packed query rows per request, or null (Q each)
   const uint8_t* blocks;             // e4m3fn bytes
   const float* scales;
   const uint32_t* lt;                // [B, max_pages]
   const uint32_t* slt;               // scale page table; == lt when absent
   const uint32_t* cache_lengths;     // [B]
-  uint16_t* out;                     // bf16 bits [B, Q, H, 512]
+  uint16_t* out;                     // bf16 bits [B, Q, H, 512], or [T, H, 512] with q_offsets
   float* ws_o;                       // split partials O   [B, RG, S, 32, 512] (fp32)
   float* ws_lse;                     // split partials lse [B, RG, S, 32]      (log2 domain)
   uint32_t* ws_flags;                // split completion words (kFlagBytes; split_merge.h)
@@ -42,7 +43,7 @@ struct DecodeArgs {
   int64_t layer_offset;              // bytes to (kv 0, layer_idx, slot 0) inside a page
   int64_t spage_stride;              // floats between pages of scales
   int64_t slayer_offset;             // floats to (kv 0, layer_idx, slot 0) inside a scale page
-  int32_t batch, q_len, num_heads, max_pages, page_size;
+  int32_t batch, q_len, num_heads, max_pages, page_size;   // q_len: the largest count with q_offsets
   int32_t row_groups, num_splits, tokens_per_split;
   int32_t grid_units;                // batch * row_groups * num_splits
   int32_t lpt;                       // 1: largest (request, split) key ranges first

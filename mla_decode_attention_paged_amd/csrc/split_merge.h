@@ -48,6 +48,7 @@
 #include <hip/hip_runtime.h>
 
 #include "mla_internal.h"
+#include "unit_order.h"
 
 namespace mla {
 namespace split_merge {
@@ -129,9 +130,9 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
-// Merge workgroups that have rows to merge in (request, row-group pair).
-__device__ __forceinline__ int merges_in_pair(const DecodeArgs& a, int pair, int nch) {
-  const int rows_total = a.q_len * a.num_heads;
+// Merge workgroups that have rows to merge in (request, row-group pair), for a
+// request of rows_total query rows.
+__device__ __forceinline__ int merges_in_pair(const DecodeArgs& a, int pair, int nch, int rows_total) {
   int n = 0;
   for (int g = 2 * pair; g < min(2 * pair + 2, a.row_groups); ++g) {
     const int rows = min(kRows, rows_total - g * kRows);
@@ -188,7 +189,8 @@ __device__ void merge_workgroup(const DecodeArgs& a, int mblock, __attribute__((
   const int ch = v % nch;
   const int rg = (v / nch) % a.row_groups;
   const int b = (v / nch) / a.row_groups;
-  const int rows_total = a.q_len * a.num_heads;
+  const RequestRows rq = request_rows(a, b);
+  const int rows_total = rq.count * a.num_heads; // this request's query rows
   const int wb = ch * nwb + wave % nwb;          // this wave's block
   const int rb = wb / kColBlocks, cb = wb % kColBlocks;
   if (rg * kRows + ((ch * nwb) / kColBlocks) * kRowBlock >= rows_total) return;   // no rows (not counted)
@@ -314,7 +316,7 @@ __device__ void merge_workgroup(const DecodeArgs& a, int mblock, __attribute__((
         hi[0] = (uint32_t)bf16_rne(acc1[0] * inv) | ((uint32_t)bf16_rne(acc1[1] * inv) << 16);
         hi[1] = (uint32_t)bf16_rne(acc1[2] * inv) | ((uint32_t)bf16_rne(acc1[3] * inv) << 16);
       }
-      uint16_t* const orow = a.out + ((size_t)b * rows_total + row) * kVDim + col0;
+      uint16_t* const orow = a.out + ((size_t)rq.first * a.num_heads + row) * kVDim + col0;
       *(mu32x2*)orow = lo;
       *(mu32x2*)(orow + 32) = hi;
     }
@@ -325,7 +327,7 @@ __device__ void merge_workgroup(const DecodeArgs& a, int mblock, __attribute__((
     uint32_t last = 0u;
     if (lane == 0)
       last = __hip_atomic_fetch_add(a.ws_flags + p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                     (uint32_t)merges_in_pair(a, rg >> 1, nch) - 1u ? 1u : 0u;
+                     (uint32_t)merges_in_pair(a, rg >> 1, nch, rows_total) - 1u ? 1u : 0u;
     if (__builtin_amdgcn_readfirstlane(last)) {
       for (int s = lane; s < nse; s += 64) __builtin_amdgcn_raw_buffer_store_b32(0u, rsrc(ready), 4 * s, 0, kScDevice);
       if (lane == 0) __hip_atomic_store(a.ws_flags + p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -96,6 +96,20 @@ __device__ __forceinline__ int workgroup_unit(const DecodeArgs& a, int rgp_count
   return item < 0 ? -1 : item * rgp_count + jx % rgp_count;   // (-1: an empty key range)
 }
 
+// The queries of request b: the packed index of its first query and its
+// query count (q_offsets, when given, holds the per-request counts as prefix
+// offsets; otherwise every request has q_len queries).  Query i, head h of
+// request b is row (first + i) * num_heads + h of q and of out.
+struct RequestRows {
+  int first, count;
+};
+__device__ __forceinline__ RequestRows request_rows(const DecodeArgs& a, int b) {
+  if (a.q_offsets == nullptr) return RequestRows{b * a.q_len, a.q_len};
+  const __attribute__((address_space(4))) uint32_t* const o = (const __attribute__((address_space(4))) uint32_t*)a.q_offsets;
+  const uint32_t first = o[b], next = o[b + 1];
+  return RequestRows{(int)first, (int)(next - first)};
+}
+
 // Grid of the decode kernels for a.
 inline int decode_grid(const DecodeArgs& a) {
   // (largest-first order: 8 * ceil(items / 8) item ranks x row-group pairs per item)

@@ -285,3 +285,20 @@ def test_binding_checks_q_len_against_q():
         binding._check_shapes(q, blocks, scales[:, :, :, :32], lt, None, cl, out, 4)
     with pytest.raises(ValueError, match="scales_lookup_table"):
         binding._check_shapes(q, blocks, scales, lt, lt[:, :2], cl, out, 4)
+
+
+def test_ragged_entry_rejects_bad_args(lib):
+    """The per-request query-count entry checks its offsets pointer and the usual
+    arguments on the host (max_q_len plays q_len's part) before any launch."""
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(7)]
+    q, offs, blocks, scales, lt, cl, out = fake
+    f = lib.mla_decode_paged_fp8_ragged
+
+    def go(offsets, max_q_len=4, shape=None, layer=0):
+        return f(q, offsets, blocks, scales, lt, None, cl, layer, max_q_len, ctypes.c_float(0.07), out,
+                 ctypes.byref(shape or good_shape()), None, 0, 0, None)
+    assert go(None) == NULL
+    assert go(ctypes.c_void_p(0x2002)) == UNSUP                # not 4-byte aligned
+    assert go(offs, max_q_len=0) == RANGE
+    assert go(offs, layer=3) == RANGE
+    assert go(offs, shape=good_shape(batch=0)) == SHAPE
