@@ -36,25 +36,26 @@ KERNEL_SRC_BF16 = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "
 UNIT_ORDER_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "unit_order.h")
 SPLIT_MERGE_SRC = os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", "split_merge.h")
 
-# HBM traffic of one main-kernel launch, from two rocprofv3 --pmc runs of
-# `bench.py --steps 5 --warmup 2 --no-cpu-baseline` (FETCH_SIZE, then
-# WRITE_SIZE, KiB per dispatch, averaged over the dispatches), each scaled by
-# what the same counter reads for a plain 1 GiB device copy
-# (`bench.py --calibrate-copy`: FETCH_SIZE 524,302.4 KiB and WRITE_SIZE
-# 1,048,576 KiB for 1,048,576 KiB moved).  The writes are the split partials
-# (workspace), not part of the algorithmic bytes.  Keyed by the SHA-256 of the
-# device code the counters were taken on (kernel_digest): any later edit of a
-# kernel makes the figure stale and bench reports traffic as null.
+# HBM traffic of one decode launch, from two rocprofv3 --pmc runs of
+# `bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-configs` (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch, averaged over the dispatches), each
+# scaled by what the same counter reads for a plain 1 GiB device copy
+# (`bench.py --calibrate-copy`: FETCH_SIZE 524,302.5 KiB and WRITE_SIZE
+# 1,048,576 KiB for 1,048,576 KiB moved).  Beyond the algorithmic bytes the
+# launch writes the split partials (workspace) and its merge workgroups read
+# them back.  Keyed by the SHA-256 of the device code the counters were taken
+# on (kernel_digest): any later edit of a kernel makes the figure stale and
+# bench reports traffic as null.
 _COPY_KIB = 1048576.0
 _FETCH_PER_KIB = 524302.5 / _COPY_KIB
 _WRITE_PER_KIB = 1048576.0 / _COPY_KIB
 MEASURED_TRAFFIC = {
-    "6ba91bb1113d5bdd519cfba6523a6d79bd6a8d2ace83039b7a639be8e89119cb": {
-        "uniform_b16_l4096": {"fetch_kib": 19945.8, "write_kib": 32834.5},
+    "c131cd7080dd45db234c3156bb0ef0f60d2e161095a1aef9f5018a304d96e300": {
+        "uniform_b16_l4096": {"fetch_kib": 36432.7, "write_kib": 34922.0},
     },
-    # unquantized (bf16) cache kernel, `bench.py --op bf16 --steps 5 --warmup 2 --no-cpu-baseline`
-    "c922b2d7e1f194d3cc7007ddec384574229a40d4fecac90a71d869bf2a7cf6ec": {
-        "uniform_bf16_b16_l4096": {"fetch_kib": 38123.3, "write_kib": 32832.0},
+    # unquantized (bf16) cache kernel, the same runs with `--op bf16`
+    "2bf2750742748aca668f1a2aeba40db19963c98c8bf90f75ee0961228e5753b6": {
+        "uniform_bf16_b16_l4096": {"fetch_kib": 54606.4, "write_kib": 34930.0},
     },
 }
 
