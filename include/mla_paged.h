@@ -191,6 +191,28 @@ mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, cons
                                          hipStream_t stream);
 
 /*
+ * mla_decode_paged_fp8_mfma8 — mla_decode_paged_fp8_profiled with the value
+ * contraction (P' V) on the block-scaled FP8 MFMA (v_mfma_scale_f32_32x32x64_
+ * f8f6f4) with the key scales folded into P' ("KVLoad2CvtProducer" page,
+ * Parameters: FP8 KV tiles): the V rows enter as their E4M3 codes, and
+ * P' = p * key scale as two
+ * E4M3 parts per element (P' = 2^e (hi + 2^-4 lo), e per query row and 32-key
+ * tile, applied through the MFMA's E8M0 operand scales).  The key
+ * contraction stays exact (bf16 MFMA on the widened codes).  Per-token
+ * scales only (scale_groups == 1): MLA_ERR_UNSUPPORTED otherwise.  Results
+ * meet the same gate as mla_decode_paged_fp8 with the inputs the tests draw,
+ * but round differently: a separate, opt-in entry point.  Arguments, plan,
+ * workspace, events and errors as for mla_decode_paged_fp8_profiled.
+ */
+mla_status mla_decode_paged_fp8_mfma8(const void* q, const void* blocks, const float* scales,
+                                      const uint32_t* lookup_table,
+                                      const uint32_t* scales_lookup_table, /* nullable */
+                                      const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                                      float softmax_scale, void* out, const mla_shape* shape,
+                                      void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                      hipEvent_t main_begin, hipEvent_t main_end, hipStream_t stream);
+
+/*
  * mla_decode_paged_fp8_ragged — mla_decode_paged_fp8_splits for requests with
  * their own query counts ("generic_get_paged_cache_with_scales" page, Args:
  * max_prompt_length is the batch's largest query length; "KVCacheScalesMHA-

@@ -39,6 +39,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 // Read-only kernel inputs read at wave-uniform addresses (page tables, cache
@@ -205,10 +208,16 @@ constexpr int kThreads = 64 * kWaveCount;
 constexpr int kEpStride = 128 + 4;            // floats per row of a value wave's epilogue transpose
 constexpr int kEpSlice = kRows * kEpStride;   // floats of one value wave's epilogue slice
 
-template <int NG>
+// F8: the value contraction on the FP8 MFMA (per-token scales only): P' per
+// tile and row group as 32 records of kF8Rec bytes, one per query row: the
+// high E4M3 parts of its 32 keys, the low parts, and the row's power-of-two
+// exponent (int32), padded so that the records spread over the LDS banks.
+constexpr int kF8Rec = 80;
+template <int NG, bool F8 = false>
 struct Layout {
+  static_assert(!F8 || NG == 1, "the FP8 value contraction serves per-token scales");
   static constexpr int kScaleBytes = NG == 1 ? 256 : 1280;      // per tile
-  static constexpr int kPBytes = NG == 1 ? 2048 : 4096;         // P' (f16) or p (fp32) per tile and group
+  static constexpr int kPBytes = F8 ? kRows * kF8Rec : NG == 1 ? 2048 : 4096;   // P' (E4M3 / f16) or p (fp32) per tile and group
   static constexpr int kXBytes = 4096;                           // a 32 x 32 fp32 partial score tile
   static constexpr int kSlots = 3;                               // steps of tiles live at once
   static constexpr int kTiles = 0;                               // kSlots steps x 2 tiles
@@ -225,7 +234,8 @@ struct Layout {
   static constexpr int kX = kMO + 8 * kRows * 4;
   static constexpr int kTotal = kX + (kXOwn ? 4 * kXBytes : 0);
 };
-static_assert(Layout<1>::kTotal <= 160 * 1024 && Layout<9>::kTotal <= 160 * 1024, "LDS budget");
+static_assert(Layout<1>::kTotal <= 160 * 1024 && Layout<9>::kTotal <= 160 * 1024 &&
+              Layout<1, true>::kTotal <= 160 * 1024, "LDS budget");
 static_assert(4 * kEpSlice * 4 <= 6 * kTileBytes, "epilogue transposes fit in the tile buffers");
 static_assert(2 * 2 * 18 * 64 * 16 <= 4 * kTileBytes, "q staging fits in the tile buffers of steps 1 and 2");
 static_assert(split_merge::lds_bytes(kThreads / 64) <= Layout<1>::kTotal &&
@@ -234,11 +244,11 @@ static_assert(split_merge::lds_bytes(kThreads / 64) <= Layout<1>::kTotal &&
 // kRecord: also write the block offsets this kernel computes to a.dbg_offsets
 // (the debug entry point's instantiation; the production one carries no such
 // code, so that its registers are not spent on it).
-template <int NG, bool kRecord>
+template <int NG, bool kRecord, bool kF8 = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 mla_decode_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  using LY = Layout<NG>;
+  using LY = Layout<NG, kF8>;
   LDS_AS char* const L0 = (LDS_AS char*)lds;
 
   const int tid = threadIdx.x;
@@ -584,7 +594,41 @@ mla_decode_kernel(DecodeArgs a) {
         }
         l_part += psum;
         LDS_AS char* pb = p_buf(i, par, d);
-        if constexpr (NG == 1) {
+        if constexpr (kF8) {
+          // P' = p * key scale, split per row against a power-of-two exponent
+          // e (the row's largest P' in this tile is m 2^(e + 8), m in [0.5, 1)):
+          // P' = 2^e (hi + 2^-4 lo) with hi = E4M3(P' 2^-e) <= 256 and lo =
+          // E4M3((P' 2^-e - hi) 2^4).  Record of row n: the 32 hi bytes in key
+          // order, the 32 lo bytes, e.  This lane holds keys 8j + 4g .. + 3.
+          float pp[16];
+          float pm = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pp[r] = p[r] * sv16[r];
+            pm = fmaxf(pm, pp[r]);
+          }
+          pm = halves_max(pm);
+          const int ex = pm > 0.0f ? max(__builtin_amdgcn_frexp_expf(pm) - 8, -120) : 0;
+          LDS_AS char* rec = pb + kF8Rec * n;
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = __builtin_amdgcn_ldexpf(pp[4 * jq + e], -ex);
+            s16x2 hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, y[0], y[1], 1.0f, false);
+            hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hw, y[2], y[3], 1.0f, true);
+            const uint32_t hu = __builtin_bit_cast(uint32_t, hw);
+            const f32x2 h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hu, 1.0f, false);
+            const f32x2 h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hu, 1.0f, true);
+            s16x2 lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, (y[0] - h01[0]) * 16.0f,
+                                                                (y[1] - h01[1]) * 16.0f, 1.0f, false);
+            lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, (y[2] - h23[0]) * 16.0f, (y[3] - h23[1]) * 16.0f,
+                                                          1.0f, true);
+            *(LDS_AS uint32_t*)(rec + 8 * jq + 4 * g) = hu;
+            *(LDS_AS uint32_t*)(rec + 32 + 8 * jq + 4 * g) = __builtin_bit_cast(uint32_t, lw);
+          }
+          if (g == 0) *(LDS_AS int*)(rec + 64) = ex;
+        } else if constexpr (NG == 1) {
           // P' = f16(p * key scale) in the A-operand order of the PV MFMA
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
@@ -778,6 +822,56 @@ mla_decode_kernel(DecodeArgs a) {
     }
   };
 
+  // F8 value contraction (per-token scales): one 32x32x64 FP8 MFMA covers
+  // both tiles of a step.  The MFMA pairs A and B bytes of the same lane half
+  // and byte, and takes the E8M0 scale of A's K block 0 (bytes 0-15 of both
+  // lane halves) for row m from lane m, of K block 1 (bytes 16-31) from lane
+  // 32 + m.  So bytes 0-15 of lane half g hold keys 16 g .. 16 g + 15 of tile
+  // 0, bytes 16-31 the same keys of tile 1, and lane (g, n) gives the
+  // exponent of tile g's row n.  P' (A) comes from the score waves' records;
+  // V (B) from transposing reads of 8 keys each: provider lane 2k + h of a
+  // 16-lane group reads key k of the 8 at columns [16 q + 8 h, + 8) of the
+  // 32-column block, and receiving lane 8 h + c gets column 16 q + 8 h + c of
+  // the 8 keys.  P' = 2^e (hi + 2^-4 lo) enters as two MFMAs whose A scales
+  // are 2^e and 2^(e - 4).
+  const int f8_kp = (lane & 15) >> 1, f8_h = lane & 1, f8_q = (lane >> 4) & 1;
+  // V read r8 (0..3) of 32-column block nb: tile r8 / 2, keys 16 g + 8 (r8 % 2) + [0, 8)
+  auto f8_vaddr = [&](int r8, int nb) __attribute__((always_inline)) -> uint32_t {
+    const int nba = 4 * vq4 + nb;                       // absolute 32-column block
+    const int key = 16 * g + 8 * (r8 & 1) + f8_kp;
+    const int c16 = 2 * (nba & 1) + f8_q;               // 16-byte column within the 64-byte block
+    return (uint32_t)(1024 * (9 * (key >> 4) + (nba >> 1)) +
+                      16 * (4 * (key & 15) + (c16 ^ (((key & 15) >> 2) & 3))) + 8 * f8_h);
+  };
+  // The 16 P' values of one tile in dwords [4 t, 4 t + 4) of hi and lo,
+  // scaled by f (the step's reference moved; rare): decode, scale, split again
+  // against an exponent moved by f's binary exponent, so that the other lane
+  // half (same row, same tile, same f) moves it alike.  Returns that move.
+  auto f8_rescale = [&](i32x8& hi, i32x8& lo, int t, float f) __attribute__((always_inline)) -> int {
+    const int dx = __builtin_amdgcn_frexp_expf(f);
+    const float fm = __builtin_amdgcn_ldexpf(f, -dx);   // in [0.5, 1)
+#pragma unroll
+    for (int w = 4 * t; w < 4 * t + 4; ++w) {
+      const f32x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)hi[w], 1.0f, false);
+      const f32x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)hi[w], 1.0f, true);
+      const f32x2 l0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)lo[w], 1.0f, false);
+      const f32x2 l1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)lo[w], 1.0f, true);
+      const float y[4] = {__builtin_fmaf(l0[0], 0.0625f, h0[0]) * fm, __builtin_fmaf(l0[1], 0.0625f, h0[1]) * fm,
+                          __builtin_fmaf(l1[0], 0.0625f, h1[0]) * fm, __builtin_fmaf(l1[1], 0.0625f, h1[1]) * fm};
+      s16x2 hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, y[0], y[1], 1.0f, false);
+      hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hw, y[2], y[3], 1.0f, true);
+      const uint32_t hu = __builtin_bit_cast(uint32_t, hw);
+      const f32x2 h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hu, 1.0f, false);
+      const f32x2 h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hu, 1.0f, true);
+      s16x2 lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, (y[0] - h01[0]) * 16.0f,
+                                                          (y[1] - h01[1]) * 16.0f, 1.0f, false);
+      lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, (y[2] - h23[0]) * 16.0f, (y[3] - h23[1]) * 16.0f, 1.0f, true);
+      hi[w] = (int)hu;
+      lo[w] = __builtin_bit_cast(int, lw);
+    }
+    return dx;
+  };
+
   // Phase 1 of a step (the score waves run their QK MFMAs): fetch the previous
   // step's tiles from LDS and do their VALU work.  Phase 2 (the score waves run
   // the softmax): the PV MFMAs.  The next step's loads go out in phase 1.
@@ -805,7 +899,87 @@ mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 2; ++r) align_step(r, i - 1, have1, mt[r], pf[r], sp[r]);
     }
-    if constexpr (NG == 1) {
+    if constexpr (kF8) {
+      // bytes 0-15 of lane half g: keys 16 g + [0, 16) of tile 0, bytes 16-31: of tile 1
+      i32x8 ahi[2], alo[2], vb8[4];
+      int ex[2][2];             // [row group][tile]
+      if (have0) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          LDS_AS const char* r0 = p_buf(i - 1, 0, r) + kF8Rec * n;
+          LDS_AS const char* r1 = p_buf(i - 1, 1, r) + kF8Rec * n;
+          const u32x4 h0 = *(LDS_AS const u32x4*)(r0 + 16 * g), l0 = *(LDS_AS const u32x4*)(r0 + 32 + 16 * g);
+          ex[r][0] = *(LDS_AS const int*)(r0 + 64);
+          u32x4 h1 = u32x4{0, 0, 0, 0}, l1 = u32x4{0, 0, 0, 0};
+          ex[r][1] = 0;
+          if (have1) {
+            h1 = *(LDS_AS const u32x4*)(r1 + 16 * g);
+            l1 = *(LDS_AS const u32x4*)(r1 + 32 + 16 * g);
+            ex[r][1] = *(LDS_AS const int*)(r1 + 64);
+          }
+          ahi[r] = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+          alo[r] = i32x8{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+          for (int r8 = 0; r8 < 4; ++r8) {
+            i32x2 w = i32x2{0, 0};
+            if (r8 < 2 || have1)
+              w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(tile_buf(i - 1, r8 >> 1) + f8_vaddr(r8, nb)));
+            vb8[nb][2 * r8] = w[0];
+            vb8[nb][2 * r8 + 1] = w[1];
+          }
+        }
+      }
+      sched_fence();
+      if (next) {
+        issue_part(i + 1, 0);
+        issue_part(i + 1, 1);
+      }
+      sched_fence();
+      int sa[2][2];             // [row group][hi, lo]: this lane's A scales (tile g)
+      if (have0) {
+        // rare: a tile's reference differs from the step's, its P' is rescaled
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if (sp[r][t] && pf[r][t] != 1.0f) {
+              // (a tile that drops below 2^-112 of the reference contributes nothing)
+              bool zero = !(pf[r][t] > 0.0f);
+              if (!zero) {
+                ex[r][t] += f8_rescale(ahi[r], alo[r], t, pf[r][t]);
+                zero = ex[r][t] < -120;
+              }
+              if (zero) {
+#pragma unroll
+                for (int w = 4 * t; w < 4 * t + 4; ++w) ahi[r][w] = alo[r][w] = 0;
+                ex[r][t] = 0;
+              }
+            }
+          }
+          const int e = g == 0 ? ex[r][0] : ex[r][1];   // in [-120, 8]
+          sa[r][0] = 127 + e;
+          sa[r][1] = 123 + e;
+        }
+      }
+      sched_fence();
+      if (next) issue_part(i + 1, 2);
+      lds_barrier();            // mid-step
+      if (have0) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            o[r][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ahi[r], vb8[nb], o[r][nb], 0, 0, 0,
+                                                                       sa[r][0], 0, 127);
+            o[r][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo[r], vb8[nb], o[r][nb], 0, 0, 0,
+                                                                       sa[r][1], 0, 127);
+          }
+        }
+      }
+    } else if constexpr (NG == 1) {
       VFrag vr0, vr1;
       PRaw pr0[2], pr1[2];
       f16x8 pa0[2][2], pa1[2][2], vb[2][4];
@@ -985,12 +1159,12 @@ int plan_merge(DecodeArgs& a, int dgrid, int waves) {
   return (int)(8 * ((units + 7) / 8));
 }
 
-template <int NG, bool kRecord>
+template <int NG, bool kRecord, bool kF8 = false>
 static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream, hipEvent_t begin, hipEvent_t end) {
   static bool attr_set = false;   // per process; the attribute is per function
-  const int lds_bytes = Layout<NG>::kTotal;
+  const int lds_bytes = Layout<NG, kF8>::kTotal;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)mla_decode_kernel<NG, kRecord>,
+    hipError_t e = hipFuncSetAttribute((const void*)mla_decode_kernel<NG, kRecord, kF8>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -999,10 +1173,10 @@ static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream, hipEvent_
   const int grid = decode_grid(a) + plan_merge(args, decode_grid(a), kThreads / 64);
   if (begin && end) {
     // the events take the kernel's own start / end timestamps
-    hipExtLaunchKernelGGL((mla_decode_kernel<NG, kRecord>), dim3(grid), dim3(kThreads), lds_bytes, stream,
+    hipExtLaunchKernelGGL((mla_decode_kernel<NG, kRecord, kF8>), dim3(grid), dim3(kThreads), lds_bytes, stream,
                           begin, end, 0, args);
   } else {
-    hipLaunchKernelGGL((mla_decode_kernel<NG, kRecord>), dim3(grid), dim3(kThreads), lds_bytes, stream, args);
+    hipLaunchKernelGGL((mla_decode_kernel<NG, kRecord, kF8>), dim3(grid), dim3(kThreads), lds_bytes, stream, args);
   }
   return hipGetLastError();
 }
@@ -1015,6 +1189,8 @@ hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stre
   if (a.dbg_offsets)
     e = scale_groups == 1 ? launch_main<1, true>(a, stream, main_begin, main_end)
                           : launch_main<9, true>(a, stream, main_begin, main_end);
+  else if (scale_groups == 1 && a.value_fp8)
+    e = launch_main<1, false, true>(a, stream, main_begin, main_end);
   else
     e = scale_groups == 1 ? launch_main<1, false>(a, stream, main_begin, main_end)
                           : launch_main<9, false>(a, stream, main_begin, main_end);

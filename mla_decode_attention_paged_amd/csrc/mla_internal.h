@@ -47,6 +47,7 @@ struct DecodeArgs {
   int32_t row_groups, num_splits, tokens_per_split;
   int32_t grid_units;                // batch * row_groups * num_splits
   int32_t lpt;                       // 1: largest (request, split) key ranges first
+  int32_t value_fp8;                 // 1: the value contraction on the FP8 MFMA (per-token scales)
   int32_t dgrid;                     // decode workgroups; the merge workgroups follow them
   int32_t merge_nwb;                 // 8-row x 64-column wave blocks per merge workgroup
   float sm_log2;                     // softmax_scale * log2(e)
