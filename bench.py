@@ -300,8 +300,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="uniform", choices=WORKLOADS)
     ap.add_argument("--splits", type=int, default=None, help="explicit split count (default: library plan)")
-    ap.add_argument("--value-fp8", action="store_true",
-                    help="the value contraction on the FP8 MFMA (mla_decode_paged_fp8_mfma8; per-token scales)")
+    ap.add_argument("--fp8-mfma", choices=["v", "kv"], default=None,
+                    help="contractions on the FP8 MFMA: v = P'V (mla_decode_paged_fp8_mfma8), kv = QK^T and P'V "
+                         "(mla_decode_paged_fp8_mfma8_kv); per-token scales")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="time only the selected workload (by default the uniform headline line also carries "
@@ -334,7 +335,7 @@ def main():
     if args.op == "append":
         bench_append(args, w)
         return
-    r = time_decode(w, args.steps, args.warmup, args.splits, args.event_every, unq, args.value_fp8)
+    r = time_decode(w, args.steps, args.warmup, args.splits, args.event_every, unq, args.fp8_mfma)
     result = {
         "metric": "MLA decode KV tokens/s + achieved GB/s & MFMA util vs roofline, 1 MI355X",
         "value": r["kv_tokens"] / (r["ms_per_step"] * 1e-3),
@@ -379,7 +380,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def time_decode(w, steps, warmup, splits, event_every, unq, value_fp8=False):
+def time_decode(w, steps, warmup, splits, event_every, unq, fp8_mfma=None):
     """Time `steps` decode calls on workload w (after `warmup` untimed ones);
     returns the step rate, the main kernel's own time and the roofline record."""
     import torch
@@ -408,7 +409,7 @@ def time_decode(w, steps, warmup, splits, event_every, unq, value_fp8=False):
             mla_decode_paged_fp8(w.q, w.blocks, w.scales, w.lookup_table, w.scales_lookup_table,
                                  w.cache_lengths, layers[i % len(layers)], w.q_len, w.softmax_scale,
                                  out=out, workspace=ws, num_splits=splits, main_events=events,
-                                 value_fp8=value_fp8)
+                                 fp8_mfma=fp8_mfma)
 
     for i in range(warmup):
         step(i)

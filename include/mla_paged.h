@@ -213,6 +213,28 @@ mla_status mla_decode_paged_fp8_mfma8(const void* q, const void* blocks, const f
                                       hipEvent_t main_begin, hipEvent_t main_end, hipStream_t stream);
 
 /*
+ * mla_decode_paged_fp8_mfma8_kv — mla_decode_paged_fp8_mfma8 with the key
+ * contraction (S = q K^T) on the block-scaled FP8 MFMA too (v_mfma_scale_f32_
+ * 16x16x128_f8f6f4; "KVLoad2CvtProducer" page, Parameters: FP8 KV tiles, with
+ * no widening stage): the key rows enter as their E4M3 codes, q (bf16) as two
+ * E4M3 parts per element with one power-of-two factor pair per query row
+ * (q = 2^a (hi + 2^-t lo)), the key scales multiply the fp32 score columns,
+ * and P' is split as in mla_decode_paged_fp8_mfma8 (here with one exponent
+ * per query row, step of 64 keys and half of the step's keys).  Per-token
+ * scales only (scale_groups == 1): MLA_ERR_UNSUPPORTED otherwise.  Results
+ * meet the same gate as mla_decode_paged_fp8 with the inputs the tests draw,
+ * but round differently: a separate, opt-in entry point.  Arguments, plan,
+ * workspace, events and errors as for mla_decode_paged_fp8_profiled.
+ */
+mla_status mla_decode_paged_fp8_mfma8_kv(const void* q, const void* blocks, const float* scales,
+                                         const uint32_t* lookup_table,
+                                         const uint32_t* scales_lookup_table, /* nullable */
+                                         const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                                         float softmax_scale, void* out, const mla_shape* shape,
+                                         void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                         hipEvent_t main_begin, hipEvent_t main_end, hipStream_t stream);
+
+/*
  * mla_decode_paged_fp8_ragged — mla_decode_paged_fp8_splits for requests with
  * their own query counts ("generic_get_paged_cache_with_scales" page, Args:
  * max_prompt_length is the batch's largest query length; "KVCacheScalesMHA-

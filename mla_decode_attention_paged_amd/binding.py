@@ -83,6 +83,8 @@ def load_library() -> ctypes.CDLL:
     lib.mla_decode_paged_fp8_profiled.restype = ctypes.c_int
     lib.mla_decode_paged_fp8_mfma8.argtypes = common + [ctypes.c_int32, vp, vp, vp]
     lib.mla_decode_paged_fp8_mfma8.restype = ctypes.c_int
+    lib.mla_decode_paged_fp8_mfma8_kv.argtypes = common + [ctypes.c_int32, vp, vp, vp]
+    lib.mla_decode_paged_fp8_mfma8_kv.restype = ctypes.c_int
     lib.mla_decode_paged_fp8_noalloc.argtypes = [vp, vp, f32p, u32p, u32p, u32p, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_float, vp, ctypes.POINTER(MlaShape), ctypes.c_int32, vp]
     lib.mla_decode_paged_fp8_noalloc.restype = ctypes.c_int
@@ -214,7 +216,7 @@ def workspace_bytes(q, blocks, scales, lookup_table, q_len, num_splits=0) -> int
 
 def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths,
                          layer_idx, q_len, softmax_scale, out=None, workspace=None, num_splits=None,
-                         main_events=None, block_offsets=None, value_fp8=False):
+                         main_events=None, block_offsets=None, fp8_mfma=None):
     """Decode attention over the paged FP8 cache; returns `out` (bf16 [B, q_len, H, 512]).
 
     q bf16 [B, q_len, H, 576]; blocks uint8 (E4M3FN bytes) [NB, KVD, NL, P, 1, 576];
@@ -229,8 +231,9 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
     block_offsets: optional int64 device tensor [B, max_blocks, 2] (debug): the
     decode kernel writes the row and scale offsets it computed for every
     16-key block it loads (mla_decode_paged_fp8_block_offsets in the C ABI).
-    value_fp8: the value contraction on the FP8 MFMA (mla_decode_paged_fp8_mfma8;
-    per-token scales only).
+    fp8_mfma: None (default), "v" (the value contraction on the FP8 MFMA,
+    mla_decode_paged_fp8_mfma8) or "kv" (both contractions,
+    mla_decode_paged_fp8_mfma8_kv); per-token scales only.
     """
     lib = load_library()
     dev = q.device
@@ -257,12 +260,14 @@ def mla_decode_paged_fp8(q, blocks, scales, lookup_table, scales_lookup_table, c
     args = (_ptr(q), _ptr(blocks), _ptr(scales), _ptr(lookup_table), _ptr(scales_lookup_table),
             _ptr(cache_lengths), int(layer_idx), int(q_len), float(softmax_scale), _ptr(out),
             ctypes.byref(shp), ws_ptr, ws_bytes)
-    if value_fp8:
+    if fp8_mfma is not None:
+        if fp8_mfma not in ("v", "kv"):
+            raise ValueError('fp8_mfma must be None, "v" or "kv"')
         if block_offsets is not None:
-            raise ValueError("value_fp8 does not combine with block_offsets")
+            raise ValueError("fp8_mfma does not combine with block_offsets")
         ev = main_events if main_events is not None else (None, None)
-        st = lib.mla_decode_paged_fp8_mfma8(*args, want, ctypes.c_void_p(ev[0]), ctypes.c_void_p(ev[1]),
-                                            _stream_handle(dev))
+        fn = lib.mla_decode_paged_fp8_mfma8 if fp8_mfma == "v" else lib.mla_decode_paged_fp8_mfma8_kv
+        st = fn(*args, want, ctypes.c_void_p(ev[0]), ctypes.c_void_p(ev[1]), _stream_handle(dev))
     elif block_offsets is not None:
         if (block_offsets.dtype != torch.int64 or block_offsets.dim() != 3 or block_offsets.shape[0] != q.shape[0]
                 or block_offsets.shape[2] != 2 or not block_offsets.is_contiguous() or block_offsets.device != dev):

@@ -3,7 +3,8 @@
     python -m mla_decode_attention_paged_amd.build
 
 Compiles csrc/mla_decode.hip (FP8 decode kernels with their split merge,
-csrc/split_merge.h, + launchers),
+csrc/split_merge.h, + launchers), csrc/mla_decode_rf.hip (the FP8 decode with
+both contractions on the block-scaled FP8 MFMA),
 csrc/mla_decode_bf16.hip (unquantized-cache decode kernel), csrc/kv_append.hip
 (append-and-quantise kernel), csrc/noalloc.hip (the decode entry point with a
 device-resident split scratch) and csrc/api.cpp (C ABI) into
@@ -34,14 +35,17 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def device_flags() -> list[str]:
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # MFMA accumulators in ordinary VGPRs: the online softmax rescales
-            # them with VALU ops, and AGPR accumulators would be copied to VGPRs
-            # and back on every loop iteration
-            "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
+def device_flags(vgpr_mfma: bool = True) -> list[str]:
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
+    if vgpr_mfma:
+        # MFMA accumulators in ordinary VGPRs: the online softmax rescales
+        # them with VALU ops, and AGPR accumulators would be copied to VGPRs
+        # and back on every loop iteration.  (The one-wave-per-SIMD kernel of
+        # mla_decode_rf.hip needs the AGPRs for its accumulators.)
+        flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    return flags
 
 
 def build(verbose: bool = False) -> str:
@@ -49,10 +53,11 @@ def build(verbose: bool = False) -> str:
     hipcc = hipcc_path()
     with tempfile.TemporaryDirectory(prefix="mla_build_") as tmp:
         objs = []
-        for src, lang in (("mla_decode.hip", "hip"), ("mla_decode_bf16.hip", "hip"), ("kv_append.hip", "hip"),
-                          ("noalloc.hip", "hip"), ("api.cpp", "c++")):
+        for src, lang in (("mla_decode.hip", "hip"), ("mla_decode_rf.hip", "hip"), ("mla_decode_bf16.hip", "hip"),
+                          ("kv_append.hip", "hip"), ("noalloc.hip", "hip"), ("api.cpp", "c++")):
             obj = os.path.join(tmp, src + ".o")
-            cmd = [hipcc, *device_flags(), "-x", lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *device_flags(src != "mla_decode_rf.hip"), "-x", lang, "-c", os.path.join(CSRC, src),
+                   "-o", obj]
             if lang == "c++":
                 # host-only source (HIP runtime calls, no kernels): hipcc still
                 # treats it as HIP, so name the one target to skip its default

@@ -158,7 +158,7 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
                        hipStream_t stream, hipEvent_t main_begin = nullptr,
                        hipEvent_t main_end = nullptr, bool unquantized = false,
                        uint64_t* dbg_offsets = nullptr, int32_t dbg_blocks = 0,
-                       const uint32_t* q_offsets = nullptr, bool value_fp8 = false) {
+                       const uint32_t* q_offsets = nullptr, int fp8_mfma = 0) {
   mla_status st = check_args(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
                              q_len, softmax_scale, out, shape, num_splits, unquantized);
   if (st != MLA_OK) return st;
@@ -213,9 +213,9 @@ mla_status decode_impl(const void* q, const void* blocks, const float* scales,
   a.lpt = (shape->batch > 1 && shape->batch <= mla::kLptMaxBatch &&
            (int64_t)shape->batch * plan.num_splits < 65536 && a.grid_units > device_cu_count()) ? 1 : 0;
   a.sm_log2 = softmax_scale * 1.4426950408889634f;
-  if (value_fp8) {
+  if (fp8_mfma) {
     if (unquantized || shape->scale_groups != 1) return MLA_ERR_UNSUPPORTED;
-    a.value_fp8 = 1;
+    a.fp8_mfma = fp8_mfma;
   }
   if (dbg_offsets) {
     // one record per 16-key block the table width can address
@@ -326,7 +326,18 @@ mla_status mla_decode_paged_fp8_mfma8(const void* q, const void* blocks, const f
                                       hipEvent_t main_end, hipStream_t stream) {
   return decode_impl(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
                      q_len, softmax_scale, out, shape, workspace, workspace_bytes, num_splits,
-                     num_splits > 0, stream, main_begin, main_end, false, nullptr, 0, nullptr, true);
+                     num_splits > 0, stream, main_begin, main_end, false, nullptr, 0, nullptr, 1);
+}
+
+mla_status mla_decode_paged_fp8_mfma8_kv(const void* q, const void* blocks, const float* scales,
+                                         const uint32_t* lookup_table, const uint32_t* scales_lookup_table,
+                                         const uint32_t* cache_lengths, int32_t layer_idx, int32_t q_len,
+                                         float softmax_scale, void* out, const mla_shape* shape, void* workspace,
+                                         size_t workspace_bytes, int32_t num_splits, hipEvent_t main_begin,
+                                         hipEvent_t main_end, hipStream_t stream) {
+  return decode_impl(q, blocks, scales, lookup_table, scales_lookup_table, cache_lengths, layer_idx,
+                     q_len, softmax_scale, out, shape, workspace, workspace_bytes, num_splits,
+                     num_splits > 0, stream, main_begin, main_end, false, nullptr, 0, nullptr, 2);
 }
 
 mla_status mla_decode_paged_fp8_block_offsets(const void* q, const void* blocks, const float* scales,

@@ -1189,7 +1189,9 @@ hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stre
   if (a.dbg_offsets)
     e = scale_groups == 1 ? launch_main<1, true>(a, stream, main_begin, main_end)
                           : launch_main<9, true>(a, stream, main_begin, main_end);
-  else if (scale_groups == 1 && a.value_fp8)
+  else if (scale_groups == 1 && a.fp8_mfma == 2)
+    e = launch_decode_rf(a, stream, main_begin, main_end);
+  else if (scale_groups == 1 && a.fp8_mfma == 1)
     e = launch_main<1, false, true>(a, stream, main_begin, main_end);
   else
     e = scale_groups == 1 ? launch_main<1, false>(a, stream, main_begin, main_end)

@@ -47,7 +47,8 @@ struct DecodeArgs {
   int32_t row_groups, num_splits, tokens_per_split;
   int32_t grid_units;                // batch * row_groups * num_splits
   int32_t lpt;                       // 1: largest (request, split) key ranges first
-  int32_t value_fp8;                 // 1: the value contraction on the FP8 MFMA (per-token scales)
+  int32_t fp8_mfma;                  // per-token scales only: 1 = P'V on the FP8 MFMA (role-split
+                                     // kernel), 2 = QK^T and P'V on it (mla_decode_rf.hip); 0 = neither
   int32_t dgrid;                     // decode workgroups; the merge workgroups follow them
   int32_t merge_nwb;                 // 8-row x 64-column wave blocks per merge workgroup
   float sm_log2;                     // softmax_scale * log2(e)
@@ -93,6 +94,11 @@ hipError_t launch_append(const AppendArgs& a, int scale_groups, hipStream_t stre
 // optional events are recorded right before / after the launch.
 hipError_t launch_decode(const DecodeArgs& a, int scale_groups, hipStream_t stream,
                          hipEvent_t main_begin = nullptr, hipEvent_t main_end = nullptr);
+
+// Launch the decode with both contractions on the block-scaled FP8 MFMA
+// (mla_decode_rf.hip; per-token scales), with its split merge.
+hipError_t launch_decode_rf(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin = nullptr,
+                            hipEvent_t main_end = nullptr);
 
 // Launch the unquantized (bf16 cache) decode kernel (with its split merge
 // when num_splits > 1).  DecodeArgs as for the FP8 kernel with blocks holding
