@@ -50,12 +50,16 @@ _COPY_KIB = 1048576.0
 _FETCH_PER_KIB = 524302.5 / _COPY_KIB
 _WRITE_PER_KIB = 1048576.0 / _COPY_KIB
 MEASURED_TRAFFIC = {
-    "c131cd7080dd45db234c3156bb0ef0f60d2e161095a1aef9f5018a304d96e300": {
-        "uniform_b16_l4096": {"fetch_kib": 36432.7, "write_kib": 34922.0},
+    "2d27722f8ac0c0e3c7ea955f1021bcddcdd0e3cfedd995ac8728712f7e56a7a6": {
+        "uniform_b16_l4096": {"fetch_kib": 36439.7, "write_kib": 34922.0},
+        "ragged_b64": {"fetch_kib": 94153.6, "write_kib": 40057.1},
+        "long_b1": {"fetch_kib": 54466.2, "write_kib": 32997.1},
+        "long_b4": {"fetch_kib": 165817.5, "write_kib": 33385.3},
+        "spec_b128": {"fetch_kib": 694760.3, "write_kib": 65536.0},
     },
     # unquantized (bf16) cache kernel, the same runs with `--op bf16`
     "2bf2750742748aca668f1a2aeba40db19963c98c8bf90f75ee0961228e5753b6": {
-        "uniform_bf16_b16_l4096": {"fetch_kib": 54606.4, "write_kib": 34930.0},
+        "uniform_bf16_b16_l4096": {"fetch_kib": 54607.4, "write_kib": 34930.0},
     },
 }
 
