@@ -148,7 +148,10 @@ typedef struct {
  * Split plans serve at most 8192 (request, row-group pair) units (larger
  * batches run unsplit), at most 4096 splits, and at most 65536 (pair,
  * split) units (the automatic plan takes fewer splits).  q values must
- * satisfy |q| <= 65504.
+ * satisfy |q| <= 65504.  Scales must be finite and non-negative, at most
+ * 255 with 64-wide groups (P' = f16(p * s) with p <= 2^8) and at most 2^15
+ * with per-token scales (the lazy threshold keeps p * s below 2^15); larger
+ * scales overflow P' to inf.
  */
 mla_status mla_decode_paged_fp8(const void* q, const void* blocks, const float* scales,
                                 const uint32_t* lookup_table,
