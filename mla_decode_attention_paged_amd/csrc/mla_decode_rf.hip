@@ -30,8 +30,9 @@
 // rows (rows 16 (w % 2) + [0, 16) of row group w / 2 of the pair) and runs the
 // whole step for them: scores of both tiles, its own online softmax, O += P' V
 // for its 16 rows x 512 columns (fp32 accumulators).  Tiles arrive by direct
-// global->LDS loads two steps ahead (three step buffers), one workgroup
-// barrier per step.
+// global->LDS loads two steps ahead (four step buffers: the loop reads the
+// keys of step j + 1 while it still reads the values of step j), one
+// workgroup barrier per step.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
