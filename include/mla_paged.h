@@ -224,10 +224,12 @@ mla_status mla_decode_paged_fp8_mfma8(const void* q, const void* blocks, const f
  * (q = 2^a (hi + 2^-t lo)), the key scales multiply the fp32 score columns,
  * and P' is split as in mla_decode_paged_fp8_mfma8 (here with one exponent
  * per query row, step of 64 keys and half of the step's keys).  Per-token
- * scales only (scale_groups == 1): MLA_ERR_UNSUPPORTED otherwise.  Results
- * meet the same gate as mla_decode_paged_fp8 with the inputs the tests draw,
- * but round differently: a separate, opt-in entry point.  Arguments, plan,
- * workspace, events and errors as for mla_decode_paged_fp8_profiled.
+ * scales only (scale_groups == 1): MLA_ERR_UNSUPPORTED otherwise.  A LOSSY
+ * mode: the FP8 MFMA's accumulation of the key contraction adds up to about
+ * one bf16 ulp to the output beyond the other entry points' error (measured
+ * up to two bf16 ulps against the exact result at |O| ~ 1.4), so it does not
+ * meet their accuracy on every input.  Arguments, plan, workspace, events
+ * and errors as for mla_decode_paged_fp8_profiled.
  */
 mla_status mla_decode_paged_fp8_mfma8_kv(const void* q, const void* blocks, const float* scales,
                                          const uint32_t* lookup_table,
