@@ -58,8 +58,8 @@ MEASURED_TRAFFIC = {
         "spec_b128": {"fetch_kib": 694760.3, "write_kib": 65536.0},
     },
     # unquantized (bf16) cache kernel, the same runs with `--op bf16`
-    "2bf2750742748aca668f1a2aeba40db19963c98c8bf90f75ee0961228e5753b6": {
-        "uniform_bf16_b16_l4096": {"fetch_kib": 54607.4, "write_kib": 34930.0},
+    "d5fceda2bc5f6edf23fa8afe69ce951795e5a070eec0603d253e0040026a0180": {
+        "uniform_bf16_b16_l4096": {"fetch_kib": 54685.0, "write_kib": 34922.0},
     },
 }
 
