@@ -57,20 +57,28 @@ __global__ void __launch_bounds__(64 * kAppendWaves) mla_append_kernel(AppendArg
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kAppendWaves + (threadIdx.x >> 6);
   if (row >= a.batch * a.q_len) return;
+  // The row's values, its cache length and its table entries are loaded with
+  // no branch between them, so that the loads overlap; a token without a
+  // table entry (or with a page id past the tensors) writes nothing.
+  const uint16_t* src = a.kv_new + (size_t)row * kHeadDim;
+  uint16_t xb[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) xb[k] = src[lane + 64 * k];
   const int b = row / a.q_len;
   const int i = row - b * a.q_len;
   const int64_t t = (int64_t)a.cache_lengths[b] - a.q_len + i;
-  if (t < 0 || t >= (int64_t)a.max_pages * a.page_size) return;   // no table entry for this token
-  const int col = (int)(t / a.page_size);
-  const int slot = (int)(t % a.page_size);
-  const uint32_t page = a.lt[(size_t)b * a.max_pages + col];
-  const uint32_t spage = a.slt[(size_t)b * a.max_pages + col];
-  if (page >= (uint32_t)a.num_blocks || spage >= (uint32_t)a.num_scale_blocks) return;
-
-  const uint16_t* src = a.kv_new + (size_t)row * kHeadDim;
+  const bool in_table = t >= 0 && t < (int64_t)a.max_pages * a.page_size;
+  const uint32_t tc = in_table ? (uint32_t)t : 0u;                   // < max_pages * page_size
+  const uint32_t col = tc / (uint32_t)a.page_size;
+  const uint32_t slot = tc - col * (uint32_t)a.page_size;
+  const size_t tix = (size_t)b * a.max_pages + col;
+  const uint32_t page = a.lt[tix];
+  const uint32_t spage = a.slt[tix];
+  const bool write = in_table && page < (uint32_t)a.num_blocks && spage < (uint32_t)a.num_scale_blocks;
+  __builtin_amdgcn_sched_barrier(0);   // (the table loads go out before any wait for the row)
   float x[9];
 #pragma unroll
-  for (int k = 0; k < 9; ++k) x[k] = __uint_as_float((uint32_t)src[lane + 64 * k] << 16);   // bf16 -> fp32, exact
+  for (int k = 0; k < 9; ++k) x[k] = __uint_as_float((uint32_t)xb[k] << 16);   // bf16 -> fp32, exact
 
   float s[9];
   if constexpr (NG == 1) {
@@ -86,13 +94,14 @@ __global__ void __launch_bounds__(64 * kAppendWaves) mla_append_kernel(AppendArg
     for (int k = 0; k < 9; ++k) s[k] = __fdiv_rn(wave_max(fabsf(x[k])), 448.0f);
   }
 
+  uint32_t code[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k)
+    code[k] = s[k] > 0.0f ? e4m3fn_rne(fminf(fmaxf(__fdiv_rn(x[k], s[k]), -448.0f), 448.0f)) : 0u;
+  if (!write) return;
   uint8_t* dst = a.blocks + (size_t)page * a.page_stride + a.layer_offset + (size_t)slot * kHeadDim;
 #pragma unroll
-  for (int k = 0; k < 9; ++k) {
-    uint32_t code = 0;
-    if (s[k] > 0.0f) code = e4m3fn_rne(fminf(fmaxf(__fdiv_rn(x[k], s[k]), -448.0f), 448.0f));
-    dst[lane + 64 * k] = (uint8_t)code;
-  }
+  for (int k = 0; k < 9; ++k) dst[lane + 64 * k] = (uint8_t)code[k];
   float* sdst = a.scales + (size_t)spage * a.spage_stride + a.slayer_offset + (size_t)slot * NG;
 #pragma unroll
   for (int k = 0; k < NG; ++k)

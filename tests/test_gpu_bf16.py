@@ -99,6 +99,36 @@ def test_q4_rows_equal_q1_calls(gpu_device):
     _q1_calls_match_q4_rows(w, run_bf16)
 
 
+def test_reference_max_jumps(gpu_device):
+    """The first 128 keys score near zero (their rows scaled by 1e-3) and later
+    keys far higher (q scaled by 8): each score wave's reference jumps
+    mid-range and the other key half's wave follows it a tile later, so the
+    value waves rescale O and the P tiles that were made against an older
+    reference (both rare paths), in one split and in the automatic plan."""
+    say("bf16 reference max jumps")
+    w = _w(gpu_device, 2, 128, [1500, 700], 64, 576, seed=91, poison=True)
+    lt = (w.lookup_table.to(torch.int64) & 0xFFFFFFFF).cpu()
+    P = w.page_size
+    for b, L in enumerate(w.lengths()):
+        for t in range(min(L, 128)):
+            w.blocks[int(lt[b, t // P]), 0, w.layer_idx, t % P, 0, :] *= 1e-3
+    w.q.mul_(8.0)
+    torch.cuda.synchronize()
+    ref = oracle_decode_unquantized(w)
+    check_gate(run_bf16(w, num_splits=1), ref, "bf16 jump, one split")
+    check_gate(run_bf16(w), ref, "bf16 jump, auto plan")
+
+
+@pytest.mark.parametrize("splits", [24, 157])
+def test_many_splits_ragged(gpu_device, splits):
+    """Many key splits (splits of one to four tiles, so the two-ahead tile
+    stream starts and drains inside a few steps) with requests that use fewer
+    splits than the plan, or one."""
+    say("bf16 many splits", splits)
+    w = _w(gpu_device, 3, 128, [20000, 3000, 5], 128, 576, seed=75, poison=True)
+    check_gate(run_bf16(w, num_splits=splits), oracle_decode_unquantized(w), f"bf16 splits {splits}")
+
+
 def test_split_partials_beyond_f16_range(gpu_device):
     """Cache rows x 2^14 and q x 2^-14: the same scores, O x 2^14, past f16's
     largest finite value; the fp32 split partials and the split merge must carry
