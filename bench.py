@@ -50,16 +50,16 @@ _COPY_KIB = 1048576.0
 _FETCH_PER_KIB = 524302.5 / _COPY_KIB
 _WRITE_PER_KIB = 1048576.0 / _COPY_KIB
 MEASURED_TRAFFIC = {
-    "2d27722f8ac0c0e3c7ea955f1021bcddcdd0e3cfedd995ac8728712f7e56a7a6": {
-        "uniform_b16_l4096": {"fetch_kib": 36439.7, "write_kib": 34922.0},
-        "ragged_b64": {"fetch_kib": 94153.6, "write_kib": 40057.1},
-        "long_b1": {"fetch_kib": 54466.2, "write_kib": 32997.1},
-        "long_b4": {"fetch_kib": 165817.5, "write_kib": 33385.3},
-        "spec_b128": {"fetch_kib": 694760.3, "write_kib": 65536.0},
+    "6ec1784b14ca62266925cd2445d84a9905ed91762797eff3c907e3045d97c29d": {
+        "uniform_b16_l4096": {"fetch_kib": 36445.6, "write_kib": 35946.0},
+        "ragged_b64": {"fetch_kib": 94158.9, "write_kib": 40045.9},
+        "long_b1": {"fetch_kib": 54476.2, "write_kib": 34021.1},
+        "long_b4": {"fetch_kib": 165822.2, "write_kib": 34409.2},
+        "spec_b128": {"fetch_kib": 694771.6, "write_kib": 65536.0},
     },
     # unquantized (bf16) cache kernel, the same runs with `--op bf16`
-    "d5fceda2bc5f6edf23fa8afe69ce951795e5a070eec0603d253e0040026a0180": {
-        "uniform_bf16_b16_l4096": {"fetch_kib": 54685.0, "write_kib": 34922.0},
+    "40a7405f768b39eb7457edf6add147d3eaef320741169275c7720d8ccfe16775": {
+        "uniform_bf16_b16_l4096": {"fetch_kib": 54683.9, "write_kib": 34922.0},
     },
 }
 

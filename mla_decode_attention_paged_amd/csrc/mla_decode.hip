@@ -1138,10 +1138,12 @@ size_t partial_bytes(int64_t batch, int64_t row_groups, int64_t num_splits) {
 }
 
 // Merge grid: units (request, row group, chunk of wave blocks); a chunk is
-// the most 8-row x 64-column wave blocks per workgroup (a power of two
-// dividing `waves`) that still gives about one merge workgroup per compute
-// unit, the remaining waves of the workgroup splitting the key splits.
-int plan_merge(DecodeArgs& a, int dgrid, int waves) {
+// the most 8-row x 64-column wave blocks per workgroup (a power of two up to
+// half a row group) that still gives about one merge workgroup per compute
+// unit.  A workgroup's waves take several blocks each when the chunk holds
+// more blocks than waves, or split the key splits of one block when it holds
+// fewer (split_merge.h).
+int plan_merge(DecodeArgs& a, int dgrid) {
   a.dgrid = dgrid;
   a.merge_nwb = 1;
   if (a.num_splits <= 1) return 0;
@@ -1152,7 +1154,11 @@ int plan_merge(DecodeArgs& a, int dgrid, int waves) {
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0) cus = c;
   }
   const int64_t groups = (int64_t)a.batch * a.row_groups;
-  int nwb = waves;
+  // as many wave blocks per workgroup as keep about one merge workgroup per
+  // compute unit (every merge workgroup holds a whole compute unit, the
+  // launch's LDS, so a larger grid queues behind itself), at most
+  // kMaxChunkBlocks: a wave merges its blocks one after the other
+  int nwb = split_merge::kMaxChunkBlocks;
   while (nwb > 1 && groups * (split_merge::kWaveBlocks / nwb) < cus) nwb >>= 1;
   a.merge_nwb = nwb;
   const int64_t units = groups * (split_merge::kWaveBlocks / nwb);
@@ -1170,7 +1176,7 @@ static hipError_t launch_main(const DecodeArgs& a, hipStream_t stream, hipEvent_
     attr_set = true;
   }
   DecodeArgs args = a;
-  const int grid = decode_grid(a) + plan_merge(args, decode_grid(a), kThreads / 64);
+  const int grid = decode_grid(a) + plan_merge(args, decode_grid(a));
   if (begin && end) {
     // the events take the kernel's own start / end timestamps
     hipExtLaunchKernelGGL((mla_decode_kernel<NG, kRecord, kF8>), dim3(grid), dim3(kThreads), lds_bytes, stream,

@@ -534,7 +534,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, hipEvent_
   const bool both = main_begin && main_end;
   if (main_begin && !both && (e = hipEventRecord(main_begin, stream)) != hipSuccess) return e;
   DecodeArgs args = a;
-  const int grid = decode_grid(a) + plan_merge(args, decode_grid(a), bf16_path::kThreadsU / 64);
+  const int grid = decode_grid(a) + plan_merge(args, decode_grid(a));
   if (both) {
     hipExtLaunchKernelGGL(bf16_path::mla_decode_bf16_kernel, dim3(grid), dim3(bf16_path::kThreadsU),
                           bf16_path::kLdsBytes, stream, main_begin, main_end, 0, args);

@@ -711,7 +711,7 @@ hipError_t launch_decode_rf(const DecodeArgs& a, hipStream_t stream, hipEvent_t 
     attr_set = true;
   }
   DecodeArgs args = a;
-  const int grid = decode_grid(a) + plan_merge(args, decode_grid(a), kThreads / 64);
+  const int grid = decode_grid(a) + plan_merge(args, decode_grid(a));
   if (begin && end) {
     hipExtLaunchKernelGGL(mla_decode_rf_kernel, dim3(grid), dim3(kThreads), kLdsTotal, stream, begin, end, 0, args);
   } else {

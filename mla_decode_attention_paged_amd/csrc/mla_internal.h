@@ -106,9 +106,9 @@ hipError_t launch_decode_rf(const DecodeArgs& a, hipStream_t stream, hipEvent_t 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin = nullptr,
                               hipEvent_t main_end = nullptr);
 
-// Merge workgroups to append to a decode grid of `waves`-wave workgroups:
-// sets a.dgrid and a.merge_ncb and returns the merge grid (0 when unsplit).
-int plan_merge(DecodeArgs& a, int dgrid, int waves);
+// Merge workgroups to append to a decode grid (of 4- or 8-wave workgroups):
+// sets a.dgrid and a.merge_nwb and returns the merge grid (0 when unsplit).
+int plan_merge(DecodeArgs& a, int dgrid);
 
 // The decode with a caller-given workspace (api.cpp), for other entry points.
 mla_status decode_with_workspace(const void* q, const void* blocks, const float* scales,

@@ -63,6 +63,11 @@ constexpr int kColBlock = 64;                    // columns per wave block (two 
 constexpr int kColBlocks = kVDim / kColBlock;    // 8
 constexpr int kRowBlock = 8;                     // rows per wave block
 constexpr int kWaveBlocks = (kRows / kRowBlock) * kColBlocks;   // 32 per row group
+// Most wave blocks per merge workgroup.  Measured on 64 ragged requests (4
+// splits, 256 row groups): 8 blocks 143.8 us, 16 blocks 138.8 us, 32 blocks
+// 140.2 us per decode launch; on the bf16 cache's 16 x 4096 keys (4-wave
+// workgroups) 4 / 8 / 16 blocks 54.5 / 52.4 / 51.9 us.
+constexpr int kMaxChunkBlocks = 16;
 constexpr int kSignalWaves = 4;                  // decode waves that write partials (per workgroup)
 constexpr uint32_t kReadyAll = 0x01010101u;      // a split's ready word once all four have
 constexpr uint32_t kSpinLimit = 1u << 19;        // polls before a merge gives up (about half a second)
@@ -169,9 +174,10 @@ __device__ __forceinline__ bool poll_ready(const uint32_t* ready, int nse, LdsU3
 // Merge workgroup `mblock` (blockIdx.x - dgrid) of a launch with kWaves
 // waves per workgroup.  A wave block is 8 rows x 64 columns of a row group
 // (32 of them per group, row-block major); a merge unit v = (request b, row
-// group rg, chunk ch) holds nwb = a.merge_nwb consecutive wave blocks, and the
-// kWaves / nwb waves on one wave block split the request's key splits
-// between them (interleaved), meeting in LDS at the end.  Units are dealt to
+// group rg, chunk ch) holds nwb = a.merge_nwb consecutive wave blocks.  With
+// fewer blocks than waves, the kWaves / nwb waves on one wave block split the
+// request's key splits between them (interleaved), meeting in LDS at the
+// end; with more, each wave merges nwb / kWaves blocks in turn.  Units are dealt to
 // XCDs in contiguous ranges, as the decode units are.  In a wave, lane (r, c)
 // owns row r of its block and columns [4c, 4c + 4) and [32 + 4c, 36 + 4c):
 // each load of the wave reads 8 rows x 128 contiguous bytes.
@@ -180,7 +186,8 @@ __device__ void merge_workgroup(const DecodeArgs& a, int mblock, __attribute__((
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwb = a.merge_nwb;                   // wave blocks per workgroup
-  const int sgp = kWaves / nwb;                  // split groups
+  const int sgp = nwb < kWaves ? kWaves / nwb : 1;   // split groups (waves per block)
+  const int bpw = nwb > kWaves ? nwb / kWaves : 1;   // blocks per wave
   const int nch = kWaveBlocks / nwb;             // chunks per row group
   const int units = a.batch * a.row_groups * nch;
   const int per_x = (units + 7) >> 3;
@@ -191,8 +198,6 @@ __device__ void merge_workgroup(const DecodeArgs& a, int mblock, __attribute__((
   const int b = (v / nch) / a.row_groups;
   const RequestRows rq = request_rows(a, b);
   const int rows_total = rq.count * a.num_heads; // this request's query rows
-  const int wb = ch * nwb + wave % nwb;          // this wave's block
-  const int rb = wb / kColBlocks, cb = wb % kColBlocks;
   if (rg * kRows + ((ch * nwb) / kColBlocks) * kRowBlock >= rows_total) return;   // no rows (not counted)
   const int nse = splits_used(a, b);
   if (nse <= 1) return;                          // the decode wrote this request's rows itself
@@ -206,119 +211,123 @@ __device__ void merge_workgroup(const DecodeArgs& a, int mblock, __attribute__((
 
   const size_t p = pair_index(a, b, rg >> 1);
   const uint32_t* const ready = a.ws_flags + kReadyWord + p * a.num_splits;
-  const int sgi = wave / nwb;
+  const int sgi = nwb < kWaves ? wave / nwb : 0;
   const int nj = sgi < nse ? (nse - sgi + sgp - 1) / sgp : 0;   // this wave's splits: sgi + j sgp
-  const int rl = rb * kRowBlock + (lane >> 3);   // row within the group
-  const int col0 = cb * kColBlock + 4 * (lane & 7);
-  const uint32_t o_off = 4 * (rl * kVDim + col0);
   const size_t pbase = ((size_t)b * a.row_groups + rg) * a.num_splits;
   const float kNegInf = -__builtin_inff();
-  float M = kNegInf, W = 0.0f;
-  mf32x4 acc0 = mf32x4{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
   bool all_ready = wave != 0;                    // wave 0 polls until every split is ready
   uint32_t polls = 0;
-  // One split at a time, in index order, with the same arithmetic whatever
-  // the order in which the splits became ready (so the result does not
-  // depend on timing): window of kBatch of this wave's splits, the loads of
-  // every ready split of the window issued at once, consumed in order.
-  auto fold = [&](float l, mf32x4 x0, mf32x4 x1) __attribute__((always_inline)) {
-    if (l > M) {
-      const float rs = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - l);
-      W *= rs;
-      acc0 *= rs;
-      acc1 *= rs;
-      M = l;
-    }
-    if (l != kNegInf) {
-      const float w = __builtin_amdgcn_exp2f(l - M);
-      W += w;
-      acc0 += w * x0;
-      acc1 += w * x1;
-    }
-  };
-  for (int w0 = 0; w0 < nj; w0 += kBatch) {
-    const int nvalid = min(kBatch, nj - w0);
-    uint32_t issued = 0;
-    int consumed = 0;
-    float ls[kBatch];
-    mf32x4 o0[kBatch], o1[kBatch];
-    while (consumed < nvalid) {
-      if (!all_ready) all_ready = poll_ready(ready, nse, mask, failed, polls, lane);
-      // ready bits of the window (lane u < nvalid looks up split sgi + (w0 + u) sgp)
-      const int sk = sgi + (w0 + lane) * sgp;
-      const bool rk = lane < nvalid &&
-                      ((__hip_atomic_load(mask + (sk >> 5), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >>
-                        (sk & 31)) & 1u);
-      const uint32_t fresh = (uint32_t)__builtin_amdgcn_ballot_w64(rk) & ~issued;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if ((fresh >> u) & 1u) {
-          const int s = sgi + (w0 + u) * sgp;
-          ls[u] = load_dev1(a.ws_lse + (pbase + s) * kRows, 4 * rl);
-          const float* const ob = a.ws_o + (pbase + s) * kRows * kVDim;
-          o0[u] = load_dev4(ob, o_off);
-          o1[u] = load_dev4(ob, o_off + 128);
-        }
+  for (int k = 0; k < bpw; ++k) {               // each block of this wave
+    const int wb = ch * nwb + (nwb < kWaves ? wave % nwb : wave + k * kWaves);   // this wave's block
+    const int rb = wb / kColBlocks, cb = wb % kColBlocks;
+    const int rl = rb * kRowBlock + (lane >> 3);   // row within the group
+    const int col0 = cb * kColBlock + 4 * (lane & 7);
+    const uint32_t o_off = 4 * (rl * kVDim + col0);
+    float M = kNegInf, W = 0.0f;
+    mf32x4 acc0 = mf32x4{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+    // One split at a time, in index order, with the same arithmetic whatever
+    // the order in which the splits became ready (so the result does not
+    // depend on timing): window of kBatch of this wave's splits, the loads of
+    // every ready split of the window issued at once, consumed in order.
+    auto fold = [&](float l, mf32x4 x0, mf32x4 x1) __attribute__((always_inline)) {
+      if (l > M) {
+        const float rs = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - l);
+        W *= rs;
+        acc0 *= rs;
+        acc1 *= rs;
+        M = l;
       }
-      issued |= fresh;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (u == consumed && ((issued >> u) & 1u)) {
-          fold(ls[u], o0[u], o1[u]);
-          ++consumed;
-        }
+      if (l != kNegInf) {
+        const float w = __builtin_amdgcn_exp2f(l - M);
+        W += w;
+        acc0 += w * x0;
+        acc1 += w * x1;
       }
-      if (consumed < nvalid && !((issued >> consumed) & 1u)) __builtin_amdgcn_s_sleep(2);
+    };
+    for (int w0 = 0; w0 < nj; w0 += kBatch) {
+      const int nvalid = min(kBatch, nj - w0);
+      uint32_t issued = 0;
+      int consumed = 0;
+      float ls[kBatch];
+      mf32x4 o0[kBatch], o1[kBatch];
+      while (consumed < nvalid) {
+        if (!all_ready) all_ready = poll_ready(ready, nse, mask, failed, polls, lane);
+        // ready bits of the window (lane u < nvalid looks up split sgi + (w0 + u) sgp)
+        const int sk = sgi + (w0 + lane) * sgp;
+        const bool rk = lane < nvalid &&
+                        ((__hip_atomic_load(mask + (sk >> 5), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >>
+                          (sk & 31)) & 1u);
+        const uint32_t fresh = (uint32_t)__builtin_amdgcn_ballot_w64(rk) & ~issued;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if ((fresh >> u) & 1u) {
+            const int s = sgi + (w0 + u) * sgp;
+            ls[u] = load_dev1(a.ws_lse + (pbase + s) * kRows, 4 * rl);
+            const float* const ob = a.ws_o + (pbase + s) * kRows * kVDim;
+            o0[u] = load_dev4(ob, o_off);
+            o1[u] = load_dev4(ob, o_off + 128);
+          }
+        }
+        issued |= fresh;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (u == consumed && ((issued >> u) & 1u)) {
+            fold(ls[u], o0[u], o1[u]);
+            ++consumed;
+          }
+        }
+        if (consumed < nvalid && !((issued >> consumed) & 1u)) __builtin_amdgcn_s_sleep(2);
+      }
     }
-  }
-  while (!all_ready) {                           // wave 0: keep publishing for the other waves
-    all_ready = poll_ready(ready, nse, mask, failed, polls, lane);
-    if (!all_ready) __builtin_amdgcn_s_sleep(2);
-  }
+    while (!all_ready) {                           // wave 0: keep publishing for the other waves
+      all_ready = poll_ready(ready, nse, mask, failed, polls, lane);
+      if (!all_ready) __builtin_amdgcn_s_sleep(2);
+    }
 
-  // every wave is past its waits; groups 1.. hand their states to group 0
-  if (sgp > 1 && sgi != 0) {
-    st[(wave * kStateFloats + 0) * 64 + lane] = M;
-    st[(wave * kStateFloats + 1) * 64 + lane] = W;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      st[(wave * kStateFloats + 2 + e) * 64 + lane] = acc0[e];
-      st[(wave * kStateFloats + 6 + e) * 64 + lane] = acc1[e];
-    }
-  }
-  __syncthreads();
-  const bool gave_up = *failed != 0u;
-  if (sgi == 0) {
-    for (int j = 1; j < sgp; ++j) {
-      const int wo = wave + j * nwb;
-      const float Mo = st[(wo * kStateFloats + 0) * 64 + lane];
-      const float Wo = st[(wo * kStateFloats + 1) * 64 + lane];
-      const float Mn = fmaxf(M, Mo);
-      const float r0 = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
-      const float r1 = Mo == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(Mo - Mn);
-      W = W * r0 + Wo * r1;
+    // every wave is past its waits; groups 1.. hand their states to group 0
+    if (sgp > 1 && sgi != 0) {
+      st[(wave * kStateFloats + 0) * 64 + lane] = M;
+      st[(wave * kStateFloats + 1) * 64 + lane] = W;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc0[e] = acc0[e] * r0 + st[(wo * kStateFloats + 2 + e) * 64 + lane] * r1;
-        acc1[e] = acc1[e] * r0 + st[(wo * kStateFloats + 6 + e) * 64 + lane] * r1;
+        st[(wave * kStateFloats + 2 + e) * 64 + lane] = acc0[e];
+        st[(wave * kStateFloats + 6 + e) * 64 + lane] = acc1[e];
       }
-      M = Mn;
     }
-    const int row = rg * kRows + rl;
-    if (row < rows_total) {
-      const float inv = W > 0.0f ? 1.0f / W : 0.0f;
-      mu32x2 lo, hi;
-      if (gave_up) {
-        lo = hi = mu32x2{0x7fc07fc0u, 0x7fc07fc0u};
-      } else {
-        lo[0] = (uint32_t)bf16_rne(acc0[0] * inv) | ((uint32_t)bf16_rne(acc0[1] * inv) << 16);
-        lo[1] = (uint32_t)bf16_rne(acc0[2] * inv) | ((uint32_t)bf16_rne(acc0[3] * inv) << 16);
-        hi[0] = (uint32_t)bf16_rne(acc1[0] * inv) | ((uint32_t)bf16_rne(acc1[1] * inv) << 16);
-        hi[1] = (uint32_t)bf16_rne(acc1[2] * inv) | ((uint32_t)bf16_rne(acc1[3] * inv) << 16);
+    __syncthreads();
+    const bool gave_up = *failed != 0u;
+    if (sgi == 0) {
+      for (int j = 1; j < sgp; ++j) {
+        const int wo = wave + j * nwb;
+        const float Mo = st[(wo * kStateFloats + 0) * 64 + lane];
+        const float Wo = st[(wo * kStateFloats + 1) * 64 + lane];
+        const float Mn = fmaxf(M, Mo);
+        const float r0 = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+        const float r1 = Mo == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(Mo - Mn);
+        W = W * r0 + Wo * r1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc0[e] = acc0[e] * r0 + st[(wo * kStateFloats + 2 + e) * 64 + lane] * r1;
+          acc1[e] = acc1[e] * r0 + st[(wo * kStateFloats + 6 + e) * 64 + lane] * r1;
+        }
+        M = Mn;
       }
-      uint16_t* const orow = a.out + ((size_t)rq.first * a.num_heads + row) * kVDim + col0;
-      *(mu32x2*)orow = lo;
-      *(mu32x2*)(orow + 32) = hi;
+      const int row = rg * kRows + rl;
+      if (row < rows_total) {
+        const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+        mu32x2 lo, hi;
+        if (gave_up) {
+          lo = hi = mu32x2{0x7fc07fc0u, 0x7fc07fc0u};
+        } else {
+          lo[0] = (uint32_t)bf16_rne(acc0[0] * inv) | ((uint32_t)bf16_rne(acc0[1] * inv) << 16);
+          lo[1] = (uint32_t)bf16_rne(acc0[2] * inv) | ((uint32_t)bf16_rne(acc0[3] * inv) << 16);
+          hi[0] = (uint32_t)bf16_rne(acc1[0] * inv) | ((uint32_t)bf16_rne(acc1[1] * inv) << 16);
+          hi[1] = (uint32_t)bf16_rne(acc1[2] * inv) | ((uint32_t)bf16_rne(acc1[3] * inv) << 16);
+        }
+        uint16_t* const orow = a.out + ((size_t)rq.first * a.num_heads + row) * kVDim + col0;
+        *(mu32x2*)orow = lo;
+        *(mu32x2*)(orow + 32) = hi;
+      }
     }
   }
   // Wave 0 counts this workgroup out (every wave of it is past its waits);
