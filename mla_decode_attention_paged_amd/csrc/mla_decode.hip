@@ -267,6 +267,22 @@ mla_decode_kernel(DecodeArgs a) {
 
   // ---- The work unit (request, row-group pair, key split) of this
   // workgroup: request order, or largest key ranges first (unit_order.h).
+  // In the largest-first order the unit is known only once the cache
+  // lengths have arrived; meanwhile the value waves touch 256 evenly spaced
+  // entries of the page tables and rows of q, so that the workgroup's first
+  // reads of them find their address translations (and many lines) warm.
+  // (Volatile reads whose values are never used: nothing waits for them
+  // until the prologue's own waits.)
+  if (a.lpt && !is_score) {
+    const int k = sub * 64 + lane;
+    const size_t nlt = (size_t)a.batch * a.max_pages;
+    (void)*(volatile const uint32_t*)(a.lt + nlt * k / 256);
+    (void)*(volatile const uint32_t*)(a.slt + nlt * k / 256);
+    if (a.q_offsets == nullptr) {
+      const size_t nrow = (size_t)a.batch * a.q_len * a.num_heads;
+      (void)*(volatile const uint32_t*)(a.q + nrow * k / 256 * kHeadDim);
+    }
+  }
   const int rgp_count = (a.row_groups + 1) >> 1;
   const int unit = workgroup_unit(a, rgp_count, L0, tid, lane, wave);
   if (unit < 0) return;

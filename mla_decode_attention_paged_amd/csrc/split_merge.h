@@ -181,13 +181,14 @@ __device__ __forceinline__ bool poll_ready(const uint32_t* ready, int nse, LdsU3
 // XCDs in contiguous ranges, as the decode units are.  In a wave, lane (r, c)
 // owns row r of its block and columns [4c, 4c + 4) and [32 + 4c, 36 + 4c):
 // each load of the wave reads 8 rows x 128 contiguous bytes.
-template <int kWaves>
-__device__ void merge_workgroup(const DecodeArgs& a, int mblock, __attribute__((address_space(3))) float* lds) {
+template <int kWaves, int kBpw>
+__device__ __forceinline__ void merge_chunk(const DecodeArgs& a, int mblock,
+                                            __attribute__((address_space(3))) float* lds) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwb = a.merge_nwb;                   // wave blocks per workgroup
   const int sgp = nwb < kWaves ? kWaves / nwb : 1;   // split groups (waves per block)
-  const int bpw = nwb > kWaves ? nwb / kWaves : 1;   // blocks per wave
+  constexpr int bpw = kBpw;                      // blocks per wave (nwb / kWaves when > 1)
   const int nch = kWaveBlocks / nwb;             // chunks per row group
   const int units = a.batch * a.row_groups * nch;
   const int per_x = (units + 7) >> 3;
@@ -342,6 +343,29 @@ __device__ void merge_workgroup(const DecodeArgs& a, int mblock, __attribute__((
       if (lane == 0) __hip_atomic_store(a.ws_flags + p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+}
+
+// The merge workgroup: chunks of more blocks than waves take the
+// multi-block form (blocks per wave fixed at compile time, so that the
+// decode path that shares the kernel keeps its register allocation).
+template <int kWaves>
+__device__ __forceinline__ void merge_workgroup(const DecodeArgs& a, int mblock,
+                                                __attribute__((address_space(3))) float* lds) {
+  static_assert(kMaxChunkBlocks % kWaves == 0 && kMaxChunkBlocks / kWaves <= 4, "chunks of 1, 2 or 4 blocks per wave");
+  const int bpw = a.merge_nwb / kWaves;          // (merge_nwb: a power of two, at most kMaxChunkBlocks)
+  if constexpr (kMaxChunkBlocks / kWaves >= 4) {
+    if (bpw == 4) {
+      merge_chunk<kWaves, 4>(a, mblock, lds);
+      return;
+    }
+  }
+  if constexpr (kMaxChunkBlocks / kWaves >= 2) {
+    if (bpw == 2) {
+      merge_chunk<kWaves, 2>(a, mblock, lds);
+      return;
+    }
+  }
+  merge_chunk<kWaves, 1>(a, mblock, lds);
 }
 
 }  // namespace split_merge

@@ -71,6 +71,7 @@ __device__ __forceinline__ int workgroup_unit(const DecodeArgs& a, int rgp_count
   const int F = tot & 0xffff, NT = tot >> 16;
   if (tid < B && tb >= 0) {
     int rank = 0;
+#pragma unroll 8
     for (int j = 0; j < B; ++j) {
       const int tj = tail[j];
       rank += (tj > tb || (tj == tb && j < tid)) ? 1 : 0;
