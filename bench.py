@@ -50,16 +50,16 @@ _COPY_KIB = 1048576.0
 _FETCH_PER_KIB = 524302.5 / _COPY_KIB
 _WRITE_PER_KIB = 1048576.0 / _COPY_KIB
 MEASURED_TRAFFIC = {
-    "6ec1784b14ca62266925cd2445d84a9905ed91762797eff3c907e3045d97c29d": {
-        "uniform_b16_l4096": {"fetch_kib": 36445.6, "write_kib": 35946.0},
-        "ragged_b64": {"fetch_kib": 94158.9, "write_kib": 40045.9},
-        "long_b1": {"fetch_kib": 54476.2, "write_kib": 34021.1},
-        "long_b4": {"fetch_kib": 165822.2, "write_kib": 34409.2},
-        "spec_b128": {"fetch_kib": 694771.6, "write_kib": 65536.0},
+    "5ceb788e19e17128e88369d2b42b66119ee0b3ea07f36ce059bfb3e57642c459": {
+        "uniform_b16_l4096": {"fetch_kib": 36450.9, "write_kib": 34922.0},
+        "ragged_b64": {"fetch_kib": 95210.4, "write_kib": 40045.9},
+        "long_b1": {"fetch_kib": 54477.6, "write_kib": 32997.1},
+        "long_b4": {"fetch_kib": 165910.9, "write_kib": 33385.2},
+        "spec_b128": {"fetch_kib": 697683.9, "write_kib": 65536.0},
     },
     # unquantized (bf16) cache kernel, the same runs with `--op bf16`
-    "40a7405f768b39eb7457edf6add147d3eaef320741169275c7720d8ccfe16775": {
-        "uniform_bf16_b16_l4096": {"fetch_kib": 54683.9, "write_kib": 34922.0},
+    "699a5e18f52f4b86b1a343740933588e79144b95a59dba51bc0fbd8b85d70f28": {
+        "uniform_bf16_b16_l4096": {"fetch_kib": 54687.7, "write_kib": 34922.0},
     },
 }
 
