@@ -4,7 +4,9 @@ A split call's workspace starts with 288 KiB of completion flags (zero
 before a buffer's first use); every call must return them to zero, so one
 workspace serves call after call, of any shape, and graph replays.  Outputs
 are compared bit for bit with the same call on a fresh workspace (the
-kernels are deterministic) and against the FP64 oracle.
+kernels are deterministic) and against the FP64 oracle, including the merge
+plan's multi-block chunks (each wave of a merge workgroup merging two or four
+wave blocks in turn) in both decode kernels.
 """
 
 import pytest
@@ -94,3 +96,31 @@ def test_graph_replays(gpu_device):
         assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
         assert int(torch.count_nonzero(ws[:FLAG_BYTES])) == 0
         run_gpu(other, num_splits=24)            # eager work between replays
+
+
+def _many_groups(gpu_device, kv_dtype, seed):
+    """32 requests x 128 heads = 128 row groups: with splits the merge plan
+    takes chunks of 16 wave blocks, so each wave of a merge workgroup merges
+    two (8-wave FP8 kernel) or four (4-wave bf16 kernel) blocks in turn."""
+    lengths = [(97 * b) % 1500 + 1 for b in range(32)]
+    lengths[5] = 0
+    return _w(gpu_device, 32, 128, lengths, 64, 576, seed=seed, poison=True, kv_dtype=kv_dtype)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_multi_block_merge_fp8(gpu_device, splits):
+    w = _many_groups(gpu_device, "fp8", 177)
+    say("multi-block merge, fp8, splits", splits)
+    check_gate(run_gpu(w, num_splits=splits), oracle_decode(w), f"fp8 multi-block merge, splits {splits}")
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_multi_block_merge_bf16(gpu_device, splits):
+    from mla_decode_attention_paged_amd import mla_decode_paged_bf16
+    from tests.oracle_inputs import oracle_decode_unquantized
+    w = _many_groups(gpu_device, "bf16", 178)
+    say("multi-block merge, bf16, splits", splits)
+    out = mla_decode_paged_bf16(w.q, w.blocks, w.lookup_table, w.cache_lengths, w.layer_idx, w.q_len,
+                                w.softmax_scale, num_splits=splits)
+    torch.cuda.synchronize()
+    check_gate(out, oracle_decode_unquantized(w), f"bf16 multi-block merge, splits {splits}")
