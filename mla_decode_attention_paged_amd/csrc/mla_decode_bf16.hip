@@ -64,6 +64,7 @@ constexpr int kSlots = 3;                        // tile buffers: two in flight,
 constexpr int kThreadsU = 512;
 constexpr int kDepthChunks = kHeadDim / 32;      // 18 MFMA k-steps of 32
 constexpr int kColBlocks = 8;                    // 16-column blocks of a value wave (128 columns)
+constexpr int kEpStride = 128 + 4;               // floats per row of a value wave's epilogue slice
 // LDS: the tile ring, then P^T per tile parity ([row block 0..3][hi, lo][64
 // lanes][16 B]), then the references per tile parity and key half ([2][2][64
 // rows]), then the score waves' final row statistics ([key half][64 rows] m,
@@ -74,6 +75,7 @@ constexpr int kAlphaOff = kPOff + 2 * kPBytes;   // 126976
 constexpr int kStatsOff = kAlphaOff + 2 * 2 * 64 * 4;
 constexpr int kLdsBytes = kStatsOff + 2 * 2 * 64 * 4;   // 129024
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(4 * kRows * kEpStride * 4 <= kSlots * kTileBytesU, "epilogue slices fit in the tile ring");
 static_assert(split_merge::lds_bytes(kThreadsU / 64) <= kLdsBytes, "merge state fits in the LDS");
 // Lazy reference maximum: the reference moves only when a score passes it by
 // more than kLazyLog2 / c2, so unnormalised weights stay below 2^kLazyLog2.
@@ -479,41 +481,62 @@ mla_decode_bf16_kernel(DecodeArgs a) {
     lds_barrier();
   }
 
-  // ---- epilogue: the rows' sums against O's references, then O / l
+  // ---- epilogue: the rows' sums against O's references, then O / l.  Each
+  // row group's 32 rows x 128 columns go through this wave's own LDS slice
+  // (the tile ring is free now), so that every store covers two rows x 128
+  // contiguous columns.
   __syncthreads();               // (the score waves' row statistics)
+  LDS_AS float* const stage = (LDS_AS float*)(L0 + sub * (kRows * kEpStride * 4));   // [32][kEpStride]
+  const int er = lane >> 5, ec = 4 * (lane & 31);   // read-back: rows 2k + er, columns ec .. ec + 3
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int row64 = 16 * rb + n;
-    float lsum = 0.0f;
+  for (int p = 0; p < 2; ++p) {
+    const int rg = 2 * rgp + p;
+    if (rg >= a.row_groups) break;           // the pair's second group does not exist
+    float lrow[2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const float mh = stat_m[hh * 64 + row64];
-      if (mh != kNegInf) lsum += stat_l[hh * 64 + row64] * exp2_fast((mh - mo[rb]) * c2);
-    }
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    const int rg = 2 * rgp + (rb >> 1);
-    const int row_in_rg = 16 * (rb & 1) + n;
-    if (rg >= a.row_groups || rg * kRows + row_in_rg >= rows_total) continue;
-    if (nsplit_eff == 1) {
-      uint16_t* orow = a.out + (row_base + rg * kRows + row_in_rg) * kVDim + 128 * sub + 4 * gq;
+    for (int h = 0; h < 2; ++h) {
+      const int rb = 2 * p + h;
+      const int row64 = 16 * rb + n;
+      float lsum = 0.0f;
 #pragma unroll
-      for (int nl = 0; nl < kColBlocks; ++nl) {
-        u32x2 packed;
-        packed[0] = f32_to_bf16_bits(o[nl][rb][0] * inv) | (f32_to_bf16_bits(o[nl][rb][1] * inv) << 16);
-        packed[1] = f32_to_bf16_bits(o[nl][rb][2] * inv) | (f32_to_bf16_bits(o[nl][rb][3] * inv) << 16);
-        *(u32x2*)(orow + 16 * nl) = packed;
+      for (int hh = 0; hh < 2; ++hh) {
+        const float mh = stat_m[hh * 64 + row64];
+        if (mh != kNegInf) lsum += stat_l[hh * 64 + row64] * exp2_fast((mh - mo[rb]) * c2);
       }
-    } else {
-      // device-scope stores that the merge workgroups read (split_merge.h)
-      const size_t pidx = ((size_t)b * a.row_groups + rg) * a.num_splits + split;
-      float* const po = a.ws_o + pidx * kRows * kVDim;
-      const uint32_t off = 4 * (row_in_rg * kVDim + 128 * sub + 4 * gq);
+      lrow[h] = lsum;
+      const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
-      for (int nl = 0; nl < kColBlocks; ++nl) split_merge::store_dev(po, off + 64 * nl, o[nl][rb] * inv);
-      if (sub == 0 && gq == 0)
-        split_merge::store_dev(a.ws_lse + pidx * kRows, 4 * row_in_rg,
-                               lsum > 0.0f ? mo[rb] * c2 + __log2f(lsum) : kNegInf);
+      for (int nl = 0; nl < kColBlocks; ++nl)
+        *(LDS_AS f32x4*)(stage + (16 * h + n) * kEpStride + 16 * nl + 4 * gq) = o[nl][rb] * inv;
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const size_t pidx = ((size_t)b * a.row_groups + rg) * a.num_splits + split;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = 2 * k + er;               // row within the group
+      if (rg * kRows + r >= rows_total) continue;
+      const f32x4 v = *(LDS_AS const f32x4*)(stage + r * kEpStride + ec);
+      if (nsplit_eff == 1) {
+        u32x2 packed;
+        packed[0] = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+        packed[1] = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        *(u32x2*)(a.out + (row_base + rg * kRows + r) * kVDim + 128 * sub + ec) = packed;
+      } else {
+        // device-scope stores that the merge workgroups read (split_merge.h)
+        split_merge::store_dev(a.ws_o + pidx * kRows * kVDim, 4 * (r * kVDim + 128 * sub + ec), v);
+      }
+    }
+    if (nsplit_eff > 1 && sub == 0 && gq == 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rb = 2 * p + h;
+        const int row_in_rg = 16 * h + n;
+        if (rg * kRows + row_in_rg < rows_total)
+          split_merge::store_dev(a.ws_lse + pidx * kRows, 4 * row_in_rg,
+                                 lrow[h] > 0.0f ? mo[rb] * c2 + __log2f(lrow[h]) : kNegInf);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // (the slice is rewritten for the next group)
   }
   if (nsplit_eff > 1) split_merge::signal_partials(a, b, rgp, split, sub, lane);   // (each of the four value waves)
 }
