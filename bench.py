@@ -343,22 +343,24 @@ def main():
     configs = None
     if not args.no_configs and not unq and args.workload == "uniform" and args.splits is None:
         # the other workloads of the same path, each timed the same way, before
-        # the headline: the headline is then timed on a GPU that has been busy
-        # for a while, at the clocks a decode loop runs at (a GPU that has been
-        # idle takes ~10 % longer per step for its first milliseconds of work)
+        # the headline, all generated and laid out first and then timed back to
+        # back, longest first: the GPU raises its clocks only after ~10-20 ms of
+        # sustained work and drops them again after ~50 ms idle, so the
+        # generation of one workload between the timings of others would
+        # leave each timed region to start on a GPU that has cooled down
+        names = ("spec", "ragged", "long1", "long4")
+        preps = {name: prepare_decode(make(name, dev), None) for name in names}
         configs = {}
-        for name in ("ragged", "long1", "long4", "spec"):
-            wc = make(name, dev)
+        for name in names:
             steps, warm = (20, 3) if name == "spec" else (50, 5)
-            rc = time_decode(prepare_decode(wc, None), steps, warm, args.event_every, False)
+            rc = time_decode(preps.pop(name), steps, warm, args.event_every, False)
             rf = rc["roofline"]
-            configs[wc.name] = {
+            configs[rc["name"]] = {
                 "kv_tokens_per_s": rc["kv_tokens"] / (rc["ms_per_step"] * 1e-3), "steps": steps,
                 "step_us": rc["ms_per_step"] * 1e3, "main_kernel_us": rf["kernel_avg_us"],
                 "after_main_us": rc["after_main_us"], "frac": rf["frac"], "step_frac": rf["step_frac"],
                 "bound": rf["bound"], "alg_flops": rf["alg_flops_per_launch"], "alg_bytes": rf["alg_bytes_per_launch"],
                 "traffic": rf["traffic"], "plan": rc["plan"]}
-            del wc   # (back to torch's cache, not freed: no idle gap before the headline)
     # the headline's layers are replicated right before it is timed (measured
     # 1-2 us per step faster than replicating them before the other workloads)
     prep = prepare_decode(w, args.splits)
@@ -482,7 +484,7 @@ def time_decode(prep, steps, warmup, event_every, unq, fp8_mfma=None):
                 "kernel_timed_launches": len(timed),
                 "alg_flops_per_launch": alg_flops, "alg_bytes_per_launch": alg_bytes,
                 "alg_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
-    return {"ms_per_step": ms_per_step, "kv_tokens": kv_tokens, "layers": len(layers), "plan": plan,
+    return {"name": w.name, "ms_per_step": ms_per_step, "kv_tokens": kv_tokens, "layers": len(layers), "plan": plan,
             "roofline": roof, "after_main_us": 1e3 * sum(after_ms) / len(after_ms)}
 
 
