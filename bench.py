@@ -121,6 +121,21 @@ def replicate_layers(w, min_bytes):
     return w2, list(range(n))
 
 
+_FLUSH = []
+
+
+def flush_infinity_cache(dev):
+    """Stream twice the Infinity Cache's capacity through it (a 512 MiB copy:
+    reads and writes), so that no data laid out before, such as the freshly
+    replicated layers, is still cached when a timed run starts."""
+    import torch
+    if not _FLUSH:
+        n = 2 * MALL_BYTES
+        _FLUSH.extend([torch.empty(n, dtype=torch.uint8, device=dev), torch.ones(n, dtype=torch.uint8, device=dev)])
+    _FLUSH[0].copy_(_FLUSH[1])
+    torch.cuda.synchronize()
+
+
 def algorithmic(w):
     """Algorithmic bytes and flops of one decode call on workload w."""
     lens = w.lengths()
@@ -437,6 +452,7 @@ def time_decode(prep, steps, warmup, event_every, unq, fp8_mfma=None):
                                  out=out, workspace=ws, num_splits=splits, main_events=events,
                                  fp8_mfma=fp8_mfma)
 
+    flush_infinity_cache(w.q.device)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
