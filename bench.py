@@ -6,7 +6,11 @@ A step is one decode call (one launch: the decode workgroups, and the split
 merge workgroups when the plan splits) over one layer of a resident multi-layer paged FP8 cache.  Consecutive steps
 decode consecutive layers, as a model's per-layer calls do; the cache holds
 enough layers (>= 512 MiB) that no step finds its layer in the 256 MB
-Infinity Cache.  Inputs are drawn once (synthetic, seeded) and stay in HBM.
+Infinity Cache, and 512 MiB are streamed through that cache before each
+timed workload's warm-up.  Inputs are drawn once (synthetic, seeded) and stay
+in HBM.  By default the ragged, long-context and speculative workloads are
+timed first, back to back, and the headline (uniform) workload last, so that
+it runs at the clocks of a busy GPU.
 
 Prints one JSON line: KV tokens/s over the whole step (value), the main
 kernel's achieved rate against its roofline (timed inside the timed region
