@@ -202,9 +202,12 @@ mla_status mla_decode_paged_fp8_profiled(const void* q, const void* blocks, cons
  * E4M3 parts per element (P' = 2^e (hi + 2^-4 lo), e per query row and 32-key
  * tile, applied through the MFMA's E8M0 operand scales).  The key
  * contraction stays exact (bf16 MFMA on the widened codes).  Per-token
- * scales only (scale_groups == 1): MLA_ERR_UNSUPPORTED otherwise.  Results
- * meet the same gate as mla_decode_paged_fp8 with the inputs the tests draw,
- * but round differently: a separate, opt-in entry point.  Arguments, plan,
+ * scales only (scale_groups == 1): MLA_ERR_UNSUPPORTED otherwise.  A LOSSY
+ * mode: P' in two E4M3 parts keeps about 8 significant bits, so most outputs
+ * are as accurate as mla_decode_paged_fp8's but some land two bf16 ulps from
+ * the exact result (measured: max normalized error 1.17e-2 on one of three
+ * seeds of 32 requests x 128 heads with up to 1,500 keys; mean error 2.7x
+ * the default path's); a separate, opt-in entry point.  Arguments, plan,
  * workspace, events and errors as for mla_decode_paged_fp8_profiled.
  */
 mla_status mla_decode_paged_fp8_mfma8(const void* q, const void* blocks, const float* scales,

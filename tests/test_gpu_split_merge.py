@@ -101,7 +101,8 @@ def test_graph_replays(gpu_device):
 def _many_groups(gpu_device, kv_dtype, seed):
     """32 requests x 128 heads = 128 row groups: with splits the merge plan
     takes chunks of 16 wave blocks, so each wave of a merge workgroup merges
-    two (8-wave FP8 kernel) or four (4-wave bf16 kernel) blocks in turn."""
+    two (the 8-wave kernels) or four (the 4-wave kernel of the FP8-MFMA "kv"
+    mode) blocks in turn."""
     lengths = [(97 * b) % 1500 + 1 for b in range(32)]
     lengths[5] = 0
     return _w(gpu_device, 32, 128, lengths, 64, 576, seed=seed, poison=True, kv_dtype=kv_dtype)
@@ -124,3 +125,15 @@ def test_multi_block_merge_bf16(gpu_device, splits):
                                 w.softmax_scale, num_splits=splits)
     torch.cuda.synchronize()
     check_gate(out, oracle_decode_unquantized(w), f"bf16 multi-block merge, splits {splits}")
+
+
+@pytest.mark.parametrize("mode", ["v", "kv"])
+def test_multi_block_merge_fp8_mfma(gpu_device, mode):
+    """The FP8-MFMA entry points with 128 row groups and 2 splits: merge
+    chunks of 16 wave blocks, two per wave in the 8-wave kernel ("v") and
+    four per wave in the 4-wave kernel ("kv", the only kernel that takes the
+    four-block form); each mode against its own bound."""
+    from tests.test_gpu_fp8_value import check, run_f8
+    w = _many_groups(gpu_device, "fp8", 179)
+    say("multi-block merge, fp8 mfma", mode)
+    check(mode, run_f8(w, mode, 2), oracle_decode(w), f"fp8 mfma {mode} multi-block merge")

@@ -19,8 +19,11 @@ base-2 scores by ~1e-2).
 Last, the FP8-MFMA option under the accumulation model measured on the
 hardware (products exact, truncated within groups of 8 terms to 13 bits below
 the group's largest): with q and P' each split into two E4M3 parts
-(compensation) both contractions stay inside the gate; PV alone on the FP8
-MFMA with P' split per tile and row passes too, and fails without the low part.
+(compensation) both contractions stay inside the gate on these cases; PV
+alone on the FP8 MFMA with P' split per tile and row passes too, and fails
+without the low part.  (The split keeps about 8 significant bits of P'; on
+larger workloads the GPU kernels of both recipes reach two bf16 ulps, so
+they ship as lossy opt-in modes with that bound: tests/test_gpu_fp8_value.py.)
 """
 
 import numpy as np
