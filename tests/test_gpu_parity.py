@@ -80,6 +80,19 @@ def test_128_heads_ragged_lengths(gpu_device, gran):
     check_gate(run_gpu(w), oracle_decode(w), f"ragged g{gran}")
 
 
+@pytest.mark.parametrize("gran", [576, 64])
+@pytest.mark.parametrize("seed", [177, 179, 181])
+def test_many_rows_several_seeds(gpu_device, gran, seed):
+    """4,096 query rows (32 requests x 128 heads, lengths spread over
+    1..1,500 keys with one empty request), default plan: every element within
+    the gate, across seeds (the worst element sits at the one-ulp floor)."""
+    say("many rows", gran, seed)
+    lengths = [(97 * b) % 1500 + 1 for b in range(32)]
+    lengths[5] = 0
+    w = _w(gpu_device, 32, 128, lengths, 64, gran, independent_scales=gran == 64, seed=seed, poison=True)
+    check_gate(run_gpu(w), oracle_decode(w), f"many rows g{gran} seed {seed}")
+
+
 @pytest.mark.parametrize("page", [16, 128])
 def test_page_sizes(gpu_device, page):
     say("page size", page)
