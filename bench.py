@@ -55,12 +55,12 @@ _COPY_KIB = 1048576.0
 _FETCH_PER_KIB = 524302.5 / _COPY_KIB
 _WRITE_PER_KIB = 1048576.0 / _COPY_KIB
 MEASURED_TRAFFIC = {
-    "ac949c479abb07df10b7e114936bc63d2492557f9c49ac10134b4dd0d40ae8aa": {
-        "uniform_b16_l4096": {"fetch_kib": 36451.1, "write_kib": 34922.0},
-        "ragged_b64": {"fetch_kib": 95214.8, "write_kib": 40045.9},
-        "long_b1": {"fetch_kib": 54476.0, "write_kib": 32997.1},
-        "long_b4": {"fetch_kib": 165886.1, "write_kib": 33385.2},
-        "spec_b128": {"fetch_kib": 697655.9, "write_kib": 65536.0},
+    "329ebabe2b27f1484e335737f2bd2331e4ead10d31b1b0ea8282cb8545381893": {
+        "uniform_b16_l4096": {"fetch_kib": 36451.3, "write_kib": 34922.0},
+        "ragged_b64": {"fetch_kib": 95204.7, "write_kib": 40045.9},
+        "long_b1": {"fetch_kib": 54476.7, "write_kib": 32997.1},
+        "long_b4": {"fetch_kib": 170616.7, "write_kib": 33385.2},
+        "spec_b128": {"fetch_kib": 697664.3, "write_kib": 65536.0},
     },
     # unquantized (bf16) cache kernel, the same runs with `--op bf16`
     "641ccc1eae71d3df27dbb8e43e4d7c38f65a6cc532418ac8f90c6233ea21a5b5": {

@@ -513,6 +513,10 @@ mla_decode_kernel(DecodeArgs a) {
       // ---- phase 1: partial scores of both row groups over depth half d:
       // accK for row group d (finished here), accG for row group 1 - d
       f32x16 accK, accG;
+      // the other tile's reference after its previous tile (written before the
+      // last end-of-step barrier): read now, its latency under the MFMAs
+      float m_other = kNegInf;
+      if (have && i > 0) m_other = alpha_buf(i - 1, par ^ 1, d)[n];
       if (have) {
         accK = f32x16{};
         accG = f32x16{};
@@ -599,7 +603,7 @@ mla_decode_kernel(DecodeArgs a) {
         // score here passes the reference by more than thr.
         LDS_AS float* ab = alpha_buf(i, par, d);
         float mref = m_run;
-        if (i > 0) mref = fmaxf(mref, alpha_buf(i - 1, par ^ 1, d)[n]);
+        mref = fmaxf(mref, m_other);
         if (wave_any(mt > mref + thr)) mref = fmaxf(mref, mt);
         if (wave_any(mref != m_run)) {
           l_part *= m_run == kNegInf ? 0.0f : exp2_fast((m_run - mref) * c2);
