@@ -16,7 +16,8 @@
 //     would skip the widening, but its internal accumulation keeps only about
 //     12 bits of the products' magnitude sum, which large scores turn into
 //     visible softmax weight errors; an FP8 P' is not accurate enough either;
-//   * the roles are split between waves (two score waves, two value waves) so
+//   * the roles are split between waves (four score waves and four value
+//     waves, one of each per SIMD) so
 //     that each keeps its operands in registers: q for the score waves, the
 //     O accumulators for the value waves;
 //   * the softmax is online, base 2, in fp32, with lazy rescaling;
